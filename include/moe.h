@@ -1,0 +1,237 @@
+/*
+ * moe.h — C ABI of libmoecache: one MoE layer's forward pass over a
+ * slot-limited expert cache, for AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes comes from the FreeToken pages:
+ *   [A] asapai.co.kr, "Running 753B GLM-5.2 on a single workstation GPU:
+ *       FreeToken doubles llama.cpp's throughput"
+ *   [B] banandre.com, "The 284B Model on a 32GB GPU Trick: How FreeToken Proves
+ *       Hardware Is a Software Problem"
+ *   [Z] zubnet.ai, news item on FreeToken and Unsloth GGUF
+ * A router picks k experts per token ([B] "Sparsity Is a Lie"); on a decode
+ * step the experts that miss the GPU cache are split by q* ~= m*B_P/B_H into
+ * experts uploaded to GPU slots and experts computed on the host CPU; the two
+ * partial sums are added after the layer ([B] "The q* Policy").  The cache is
+ * one LRU over all layers, updated on misses, starting empty ([A] "Abandoning
+ * fixed offloading ...", [B] "Semantic-Aware Caching", [B] "Elastic Memory").
+ * Prefill streams whole layers through two device buffers ([A] same section).
+ *
+ * Conventions (all entry points):
+ *   - Return an int status (MOE_OK = 0, negative on error).  Nothing aborts and
+ *     no C++ exception crosses the ABI.  A call that returns an error has no side
+ *     effect on the context, the cache or any output (inputs are validated first).
+ *   - The caller owns every buffer (device memory from hipMalloc or torch, host
+ *     memory from hipHostMalloc or pinned torch tensors).  The library owns only
+ *     the context, its cache state and its HIP events.
+ *   - d_ = device pointer, h_ = host pointer.  GPU calls are asynchronous on the
+ *     given stream; faults in asynchronous work surface at the caller's sync.
+ *   - A context is not thread-safe.  Results are bitwise deterministic run to
+ *     run (no floating-point atomics).
+ *   - Element formats: weights fp32, bf16 or MXFP4 (OCP MX v1.0: e2m1 codes,
+ *     element 2i in the low nibble of byte i, one e8m0 scale per 32 elements
+ *     along K); activations and outputs are fp32 for fp32 weights and bf16
+ *     otherwise; router logits, gates and partial sums are fp32.
+ */
+#ifndef MOE_CACHE_H
+#define MOE_CACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status codes */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)        /* bad argument (null pointer, out-of-range id, NaN scale) */
+#define MOE_ESHAPE (-2)        /* shape not supported by the config or the kernels */
+#define MOE_ECAPACITY (-3)     /* caller array too small */
+#define MOE_EHIP (-4)          /* a HIP runtime call failed; moe_last_error has its string */
+#define MOE_EUNSUPPORTED (-5)  /* valid request that this build does not implement */
+#define MOE_ESTATE (-6)        /* pools not bound, or a call out of order */
+
+/* weight element formats */
+#define MOE_W_F32 0
+#define MOE_W_BF16 1
+#define MOE_W_MXFP4 2
+
+/* integer readings of q* ~= m*B_P/B_H ([B] "The q* Policy") */
+#define MOE_Q_NEAREST 0  /* floor((m*B_P)/B_H + 1/2) in IEEE double, clamped to [0, m] */
+#define MOE_Q_ARGMIN 1   /* smallest q minimising max(q/B_P, (m-q)/(B_H-B_P)) */
+
+typedef struct moe_config {
+    int32_t hidden;        /* H: model width; multiple of 64 (of 256 for MXFP4) */
+    int32_t inter;         /* I: expert intermediate width; multiple of 32 */
+    int32_t n_experts;     /* E: routed experts per layer, 1..512 */
+    int32_t top_k;         /* k: experts per token, 1..min(E, 16) */
+    int32_t n_shared;      /* 0 or 1 always-on shared expert (gate 1, never cached) */
+    int32_t n_slots;       /* C: device expert slots of the global LRU cache (>= 0) */
+    int32_t n_layers;      /* layers sharing the cache, key = (layer, expert); >= 1 */
+    int32_t w_dtype;       /* MOE_W_F32 | MOE_W_BF16 | MOE_W_MXFP4 */
+    int32_t renormalize;   /* 1: gates are the softmax renormalised over the top k;
+                              0: softmax over all E experts */
+    int32_t q_round;       /* MOE_Q_NEAREST | MOE_Q_ARGMIN */
+    double bp_gbps;        /* B_P: host->GPU link bandwidth (e.g. 52.7) */
+    double bh_gbps;        /* B_H: host memory bandwidth available to experts (e.g. 77.3) */
+} moe_config;
+
+/* One decode step's cache plan ([B] "The q* Policy"; [A] "Abandoning fixed
+ * offloading ...").  The caller allocates every array; each set array needs
+ * `cap` >= the number of distinct experts of the step (min(E, T*k) suffices),
+ * slot_of_expert needs E entries (it may be NULL).  All sets are in step order:
+ * more tokens first, then lower expert id. */
+typedef struct moe_plan {
+    int32_t cap;
+    int32_t n_distinct;       /* |S_t| */
+    int32_t n_hit;
+    int32_t n_miss;           /* m */
+    int32_t n_fill;           /* q = min(q*(m), C - n_hit) */
+    int32_t n_host;           /* m - q */
+    int32_t layer;
+    int32_t* distinct;        /* [cap] S_t */
+    int32_t* hit;             /* [cap] resident experts */
+    int32_t* hit_slot;        /* [cap] their slots */
+    int32_t* fill;            /* [cap] misses uploaded to the GPU (first q misses) */
+    int32_t* fill_slot;       /* [cap] destination slots */
+    int32_t* fill_victim;     /* [cap] evicted cache key (layer*E + expert), -1 for a free slot */
+    int32_t* host;            /* [cap] misses computed on the CPU (not inserted) */
+    int32_t* slot_of_expert;  /* [E] this layer's slot table after the step, -1 = absent */
+} moe_plan;
+
+typedef struct moe_stats {
+    int64_t steps;
+    int64_t distinct;        /* distinct (expert, step) reads */
+    int64_t hits;
+    int64_t misses;
+    int64_t fills;
+    int64_t host;
+    int64_t evictions;
+} moe_stats;
+
+typedef struct moe_ctx moe_ctx;
+
+/* ---------------------------------------------------------------- context */
+/* Validate *cfg and create a context.  Makes no HIP call (usable on a host
+ * without a GPU for the planner and the host FFN).  Errors: MOE_EINVAL (null),
+ * MOE_ESHAPE (sizes), MOE_EUNSUPPORTED (dtype).  *out is NULL on error. */
+int moe_create(const moe_config* cfg, moe_ctx** out);
+/* Free the context and its HIP events; NULL is a no-op.  Never frees caller memory. */
+void moe_destroy(moe_ctx* ctx);
+/* Message of the last failed call on ctx (owned by ctx, valid until the next call). */
+const char* moe_last_error(const moe_ctx* ctx);
+/* Static name of a status code. */
+const char* moe_status_string(int status);
+
+/* Bytes of one expert blob (the slot stride; a multiple of 256), or a negative
+ * status for an invalid config.  The blob is the library's own layout, the same
+ * in the host pool and in the device slots, so a fill is one contiguous copy
+ * ([B] "Elastic Memory": experts are read into their final host layout). */
+int64_t moe_expert_bytes(const moe_config* cfg);
+/* Device scratch bytes needed by moe_route + moe_expert_ffn for up to max_T tokens. */
+int64_t moe_workspace_bytes(const moe_config* cfg, int32_t max_T);
+/* Rows of the pair-output buffer d_o for T tokens: T*k (+ T with a shared expert). */
+int64_t moe_pair_rows(const moe_config* cfg, int32_t T);
+
+/* Pack one expert from natural layout into a blob (host memory, moe_expert_bytes).
+ *   fp32 / bf16: wg, wu [I][H] and wd [H][I] row-major, elements float or bf16 bits;
+ *                sg, su, sd must be NULL.
+ *   MXFP4:       wg, wu [I][H/2] and wd [H][I/2] code bytes; sg, su [I][H/32] and
+ *                sd [H][I/32] e8m0 scales (0xFF = NaN is rejected: MOE_EINVAL). */
+int moe_pack_expert(const moe_config* cfg, const void* wg, const void* wu, const void* wd,
+                    const uint8_t* sg, const uint8_t* su, const uint8_t* sd, void* blob);
+
+/* Bind the pools used by moe_fill and moe_host_ffn.
+ *   d_slots: device, n_slots blobs (n_slots <= cfg->n_slots);
+ *   h_pool:  host (pinned for asynchronous fills), n_pool = n_layers*E blobs in
+ *            key order (layer*E + expert).
+ * Either pointer may be NULL when the corresponding calls are not used.  Makes no
+ * HIP call (the fill event is created by the first moe_fill / moe_upload). */
+int moe_bind_pools(moe_ctx* ctx, void* d_slots, int32_t n_slots, const void* h_pool, int32_t n_pool);
+
+/* ---------------------------------------------------------------- router */
+/* Softmax + top-k and token-by-expert permutation of T tokens (async on s).
+ *   d_logits [T][E] fp32 (finite; NaN order is unspecified);
+ *   d_topk_ids [T][k] int32 (logit descending, lower id first on equal logits);
+ *   d_topk_w [T][k] fp32 gates; d_counts [E]; d_offsets [E+1] exclusive prefix
+ *   sums; d_perm [T*k] pair ids p = t*k + j grouped by expert, ascending p within
+ *   an expert; d_inv [T*k] with inv[perm[i]] = i.  d_ws: moe_workspace_bytes.
+ *   T == 0 is a valid no-op.  ([B] "Sparsity Is a Lie") */
+int moe_route(moe_ctx* ctx, const float* d_logits, int32_t T, int32_t* d_topk_ids, float* d_topk_w,
+              int32_t* d_counts, int32_t* d_offsets, int32_t* d_perm, int32_t* d_inv, void* d_ws,
+              hipStream_t s);
+
+/* ---------------------------------------------------------------- cache planner (host) */
+/* q* for m misses ([B] "The q* Policy").  Pure; negative m gives 0. */
+int32_t moe_qstar(int32_t m, double bp, double bh, int32_t rounding);
+/* Plan one decode step of `layer` from the host copy of its top-k ids
+ * h_topk_ids [T][k] and update the cache: hits, q* fills (evicting the least
+ * recently used expert not used in this step), host set.  Synchronous, host only.
+ * Errors (no state change): MOE_EINVAL (ids out of range or repeated within a
+ * token, bad layer), MOE_ECAPACITY (plan->cap too small). */
+int moe_lru_step(moe_ctx* ctx, int32_t layer, const int32_t* h_topk_ids, int32_t T, moe_plan* plan);
+/* Replay n_steps decode steps (ids [n_steps][T][k]) in order; plans may be NULL
+ * (then only *stats is filled), else an array of n_steps plans.  stats may be NULL.
+ * All ids are validated before the cache is touched. */
+int moe_lru_replay(moe_ctx* ctx, int32_t layer, const int32_t* h_topk_ids, int32_t n_steps, int32_t T,
+                   moe_plan* plans, moe_stats* stats);
+/* Empty the cache (cold start) and zero the statistics. */
+int moe_lru_reset(moe_ctx* ctx);
+/* This layer's current slot table (h_slot_of_expert [E], -1 = absent). */
+int moe_lru_slots(const moe_ctx* ctx, int32_t layer, int32_t* h_slot_of_expert);
+/* Cumulative statistics since create/reset. */
+int moe_lru_stats(const moe_ctx* ctx, moe_stats* stats);
+
+/* ---------------------------------------------------------------- miss fills */
+/* Upload the plan's fills from the bound host pool into the bound device slots:
+ * one hipMemcpyAsync per fill on `side`, then the context's fill event is
+ * recorded on `side` ([B] "The q* Policy": copy the weights across PCIe and
+ * execute on the GPU).  Requires moe_bind_pools with both pools. */
+int moe_fill(moe_ctx* ctx, const moe_plan* plan, hipStream_t side);
+/* Make stream s wait for the last moe_fill / moe_upload of this context. */
+int moe_fill_wait(moe_ctx* ctx, hipStream_t s);
+/* Asynchronous copy of `bytes` from host to device on `side` followed by the
+ * fill event (whole-layer streaming into a prefill buffer, [A] "Abandoning fixed
+ * offloading ...": full-layer double buffering). */
+int moe_upload(moe_ctx* ctx, void* d_dst, const void* h_src, int64_t bytes, hipStream_t side);
+
+/* ---------------------------------------------------------------- expert FFN */
+/* GPU SwiGLU experts over device slots (async on s):
+ *   o[p] = Wd_e (silu(Wg_e x_t) * (Wu_e x_t)) for every pair p = t*k + j whose
+ *   expert e = topk_ids[t][j] is listed in h_experts, read from the blob at
+ *   d_slot_base + h_slots[i]*moe_expert_bytes; with with_shared = 1 also
+ *   o[T*k + t] for the shared expert blob d_shared (all tokens).
+ *   d_x [T][H] activations; d_offsets, d_perm from moe_route; h_experts /
+ *   h_slots: host arrays of n (<= E) distinct expert ids and slot indices;
+ *   d_o [moe_pair_rows][H] fp32 (rows of unlisted experts are not written);
+ *   d_ws: moe_workspace_bytes(max_T >= T).
+ * T <= 8 runs the decode path (HBM-bound batched GEMV); larger T runs the
+ * grouped GEMM on MFMA.  Errors: MOE_EINVAL (ids, null), MOE_ESHAPE. */
+int moe_expert_ffn(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* d_offsets,
+                   const int32_t* d_perm, const void* d_slot_base, const int32_t* h_experts,
+                   const int32_t* h_slots, int32_t n, const void* d_shared, int32_t with_shared,
+                   float* d_o, void* d_ws, hipStream_t s);
+
+/* CPU SwiGLU experts of the plan's host set from the bound host pool:
+ * h_y[t] = sum over j with topk_ids[t][j] in plan->host of w[t][j]*FFN(x_t),
+ * fp32 [T][H] (fully written; zero rows where nothing is on the host), with
+ * n_threads worker threads (<= 0: hardware concurrency).  ([B] "The q* Policy":
+ * leave the weights in system RAM and execute on the CPU.)  Synchronous. */
+int moe_host_ffn(moe_ctx* ctx, const void* h_x, int32_t T, const int32_t* h_topk_ids,
+                 const float* h_topk_w, const moe_plan* plan, float* h_y, int32_t n_threads);
+
+/* ---------------------------------------------------------------- merge */
+/* Gate-weighted un-permute and exact merge of the partial sums (async on s):
+ *   out[t] = cast( sum_{j=0..k-1, topk_ids[t][j] in h_gpu_experts} w[t][j]*o[t*k+j]
+ *                  + (with_shared ? o[T*k+t] : 0) + (d_y_host ? y_host[t] : 0) )
+ * in fp32, in that order; out is fp32 (fp32 weights) or bf16 [T][H].
+ * ([B] "The q* Policy": the partial sums merge exactly after the layer.) */
+int moe_merge_partial(moe_ctx* ctx, const float* d_o, const int32_t* d_topk_ids, const float* d_topk_w,
+                      const int32_t* h_gpu_experts, int32_t n_gpu, int32_t with_shared,
+                      const float* d_y_host, int32_t T, void* d_out, hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_CACHE_H */

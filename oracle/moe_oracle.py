@@ -50,7 +50,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "bf16_bits_to_f64", "round_to_bf16", "mxfp4_decode", "expert_f64",
+    "bf16_bits_to_f64", "round_to_bf16", "mxfp4_decode", "expert_f64", "act_f64",
     "router_logits", "route", "permute", "silu", "expert_ffn", "moe_layer",
     "moe_layer_partitioned", "qstar", "step_order", "LRUCache", "mattson_misses",
     "stream_time", "prefill_pipeline_time", "E2M1_VALUES",

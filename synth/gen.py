@@ -37,7 +37,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "workload", "seed_root", "bf16_bits_from_f32",
     "f32_from_bf16_bits", "expert_weights", "shared_expert_weights",
-    "activations", "iid_logits", "zipf_reuse_trace", "mxfp4_quantize",
+    "activations", "iid_logits", "expert_weights_many", "zipf_reuse_trace", "mxfp4_quantize",
     "router_weights", "trace_stats",
 ]
 
@@ -94,39 +94,43 @@ def _rng(wl_or_seed, *key) -> np.random.Generator:
 # ---------------------------------------------------------------- formats
 def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (nearest, ties to even); returns uint16 bit patterns."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = u + 0x7FFF + ((u >> 16) & 1)
-    return (u >> 16).astype(np.uint16)
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    u = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))   # finite inputs: no wrap-around
+    return (u >> np.uint32(16)).astype(np.uint16)
 
 
 def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-_E2M1_MID = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+_E2M1_MID = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
 
 
 def mxfp4_quantize(w: np.ndarray):
     """OCP MX v1.0 conversion of fp32 rows [R, K] (K % 32 == 0) to MXFP4.
 
-    Returns (codes uint8 [R, K/2] with the even element in the low nibble,
-    scales uint8 [R, K/32] holding the e8m0 biased exponent)."""
+    Shared exponent X = floor(log2(amax)) - 2 of each block of 32 (from frexp, so
+    exact), elements |w| / 2^X rounded to the nearest e2m1 magnitude with ties to
+    the even code, saturating at 6.  Returns (codes uint8 [R, K/2] with the even
+    element in the low nibble, scales uint8 [R, K/32] = X + 127)."""
     w = np.asarray(w, dtype=np.float32)
     R, K = w.shape
     assert K % 32 == 0
-    blk = w.reshape(R, K // 32, 32).astype(np.float64)
+    blk = w.reshape(R, K // 32, 32)
     amax = np.abs(blk).max(axis=2)
-    with np.errstate(divide="ignore"):
-        x = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    _, ex = np.frexp(amax)                      # amax = m * 2^ex, m in [0.5, 1)
+    x = np.where(amax > 0, ex.astype(np.int32) - 1 - 2, -127)
     x = np.clip(x, -127, 127)
-    scaled = np.abs(blk) / np.exp2(x)[:, :, None]
-    idx = np.searchsorted(_E2M1_MID, scaled, side="left")
-    at_mid = np.zeros_like(idx, dtype=bool)
-    inb = idx < len(_E2M1_MID)
-    at_mid[inb] = scaled[inb] == _E2M1_MID[idx[inb]]
-    idx = np.where(at_mid & (idx % 2 == 1), idx + 1, idx)
+    scaled = np.ldexp(np.abs(blk), (-x)[:, :, None])
+    idx = np.zeros(scaled.shape, dtype=np.uint8)
+    tie_odd = np.zeros(scaled.shape, dtype=bool)
+    for i, mid in enumerate(_E2M1_MID):
+        idx += scaled > mid
+        if i % 2 == 1:
+            tie_odd |= scaled == mid
+    idx += tie_odd
     idx = np.minimum(idx, 7)
-    code = (idx | np.where(np.signbit(blk), 8, 0)).astype(np.uint8).reshape(R, K)
+    code = (idx | np.where(np.signbit(blk), np.uint8(8), np.uint8(0))).reshape(R, K)
     codes = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
     scales = (x + 127).astype(np.uint8)
     return codes, scales
@@ -157,6 +161,14 @@ def expert_weights(wl: Workload, e: int) -> dict:
     cu, su = mxfp4_quantize(wu)
     cd, sd = mxfp4_quantize(wd)
     return {"wg": cg, "wu": cu, "wd": cd, "sg": sg, "su": su, "sd": sd}
+
+
+def expert_weights_many(wl: Workload, experts, threads: int = 8) -> dict:
+    """expert_weights for several experts, drawn on a thread pool (numpy releases the GIL)."""
+    import concurrent.futures as cf
+    experts = list(experts)
+    with cf.ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        return dict(zip(experts, ex.map(lambda e: expert_weights(wl, e), experts)))
 
 
 def shared_expert_weights(wl: Workload):

@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Integer outputs (top-k ids, counts, offsets, permutation and its inverse, cache
+plans) must match bit for bit; gates within 1e-6 relative; layer outputs within
+the per-token relative error max|y - y_ref| / max|y_ref| of 1e-5 (fp32) or 2e-2
+(bf16, MXFP4), with a tighter secondary bound where the arithmetic allows it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import Experts, TOL, config, rel_err_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from expert_cached_moe_amd import binding
+    return binding
+
+
+def _dev_act(x):
+    """Activations to the device: fp32 as is, bf16 bits as int16 storage."""
+    if x.dtype == np.float32:
+        return torch.from_numpy(x).cuda()
+    return torch.from_numpy(x.view(np.int16)).cuda()
+
+
+def _out_f64(t, wl, T):
+    a = t.cpu().numpy()
+    if wl.act_dtype == "f32":
+        return a.reshape(T, wl.H).astype(np.float64)
+    return oracle.bf16_bits_to_f64(a.view(np.uint16)).reshape(T, wl.H)
+
+
+def _route_case(B, wl, logits, renorm=1):
+    from expert_cached_moe_amd.runtime import LayerBuffers
+    T = logits.shape[0]
+    cfg = config(wl, renormalize=renorm)
+    L = LayerBuffers(cfg, max(T, 1))
+    dl = torch.from_numpy(np.ascontiguousarray(logits, np.float32)).cuda() if T else torch.empty(1).cuda()
+    L.route(dl, T)
+    torch.cuda.synchronize()
+    n = T * wl.k
+    ids = L.ids[:n].cpu().numpy().reshape(T, wl.k)
+    w = L.w[:n].cpu().numpy().reshape(T, wl.k)
+    counts, offsets = L.counts.cpu().numpy(), L.offsets.cpu().numpy()
+    perm, inv = L.perm[:n].cpu().numpy(), L.inv[:n].cpu().numpy()
+    rids, rg = oracle.route(logits, wl.k, renormalize=bool(renorm)) if T else (np.zeros((0, wl.k), np.int32), None)
+    rc, ro, rp, ri = oracle.permute(rids, wl.E)
+    assert np.array_equal(ids, rids)
+    assert np.array_equal(counts, rc) and np.array_equal(offsets, ro)
+    assert np.array_equal(perm, rp) and np.array_equal(inv, ri)
+    if T:
+        assert np.abs(w - rg).max() <= 1e-6 * np.abs(rg).max() + 1e-12
+    L.close()
+
+
+@pytest.mark.parametrize("case", ["tiny", "a3b_b1", "a3b_b8", "v4_b8", "prefill_a3b", "prefill_v4", "ragged513",
+                                  "t1", "t0", "ties", "no_renorm", "e8_k8"])
+def test_route_parity(B, case):
+    print(f"[route] {case}", flush=True)
+    if case == "tiny":
+        wl = synth.workload("tiny_fp32")
+        logits = oracle.router_logits(synth.activations(wl, wl.T), synth.router_weights(wl))
+        _route_case(B, wl, logits)
+    elif case in ("a3b_b1", "a3b_b8"):
+        wl = synth.workload("a3b_decode_bf16")
+        b = 1 if case == "a3b_b1" else 8
+        lg, _ = synth.zipf_reuse_trace(wl, b, 16)
+        for s in range(16):
+            _route_case(B, wl, lg[s])
+    elif case == "v4_b8":
+        wl = synth.workload("v4flash_decode_bf16")
+        lg, _ = synth.zipf_reuse_trace(wl, 8, 8)
+        for s in range(8):
+            _route_case(B, wl, lg[s])
+    elif case == "prefill_a3b":
+        wl = synth.workload("a3b_prefill8k_bf16")
+        _route_case(B, wl, synth.iid_logits(wl, 8192))
+    elif case == "prefill_v4":
+        wl = synth.workload("v4flash_mxfp4")
+        _route_case(B, wl, synth.iid_logits(wl, 8192))
+    elif case == "ragged513":
+        wl = synth.workload("a3b_prefill8k_bf16")
+        _route_case(B, wl, synth.iid_logits(wl, 513, tag=5))       # 4104 pairs: multi-chunk path, ragged tail
+    elif case == "t1":
+        wl = synth.workload("v4flash_mxfp4")
+        _route_case(B, wl, synth.iid_logits(wl, 1, tag=2))
+    elif case == "t0":
+        wl = synth.workload("a3b_decode_bf16")
+        _route_case(B, wl, np.zeros((0, wl.E), np.float32))
+    elif case == "ties":
+        wl = synth.workload("a3b_prefill8k_bf16")
+        rng = np.random.default_rng(4)
+        lg = (rng.integers(-3, 3, size=(700, wl.E)) * 0.5).astype(np.float32)
+        lg[::7] = 0.0
+        lg[1::7] = -0.0
+        _route_case(B, wl, lg)
+    elif case == "no_renorm":
+        wl = synth.workload("v4flash_decode_bf16")
+        _route_case(B, wl, synth.iid_logits(wl, 37, tag=3), renorm=0)
+    elif case == "e8_k8":
+        import dataclasses
+        wl = dataclasses.replace(synth.workload("tiny_fp32"), k=8)
+        _route_case(B, wl, np.random.default_rng(0).standard_normal((9, 8)).astype(np.float32))
+
+
+class GpuLayer:
+    """Device pool of packed experts (slot = position in ``experts``) and buffers."""
+
+    def __init__(self, B, wl, experts, max_T, ex=None):
+        from expert_cached_moe_amd.runtime import LayerBuffers, pack_pool
+        self.wl, self.ex = wl, ex or Experts(wl)
+        self.cfg = config(wl)
+        self.L = LayerBuffers(self.cfg, max_T)
+        self.experts = list(experts)
+        self.slot = {e: i for i, e in enumerate(self.experts)}
+        self.ex.prefetch(self.experts + ([wl.E] if wl.n_shared else []))
+        host = pack_pool(self.cfg, [self.ex.raw(e) for e in self.experts], pin=False)
+        self.pool = host.cuda()
+        self.shared = None
+        if wl.n_shared:
+            self.shared = pack_pool(self.cfg, [self.ex.raw(wl.E)], pin=False).cuda()
+
+    def run(self, logits, x, gpu_experts, with_shared, y_host=None):
+        T = logits.shape[0]
+        wl, L = self.wl, self.L
+        L.route(torch.from_numpy(np.ascontiguousarray(logits)).cuda(), T)
+        dx = _dev_act(x)
+        slots = [self.slot[e] for e in gpu_experts]
+        L.ffn(dx, T, self.pool, gpu_experts, slots, self.shared, with_shared)
+        out = torch.empty(T * wl.H, dtype=torch.float32 if wl.act_dtype == "f32" else torch.int16, device="cuda")
+        L.merge(gpu_experts, with_shared, y_host, T, out)
+        torch.cuda.synchronize()
+        return out
+
+
+def _decode_case(B, name, T, frac, seed):
+    wl = synth.workload(name)
+    lg, _ = synth.zipf_reuse_trace(wl, T, 3, tag=seed)
+    logits = lg[2]
+    ids, gates = oracle.route(logits, wl.k)
+    present = sorted(set(ids.ravel().tolist()))
+    rng = np.random.default_rng(seed)
+    gpu = sorted(rng.permutation(present)[: max(1, int(round(frac * len(present))))].tolist())
+    # slots in a shuffled order with unused slots between them
+    pool_order = rng.permutation(present + [e for e in range(wl.E) if e not in present][:3]).tolist()
+    G = GpuLayer(B, wl, pool_order, T)
+    x = synth.activations(wl, T, tag=seed)
+    ws = 1 if wl.n_shared else 0
+    out = G.run(logits, x, gpu, ws)
+    y = _out_f64(out, wl, T)
+    xf = oracle.act_f64(x, wl.act_dtype)
+    g32 = G.L.w[: T * wl.k].cpu().numpy().reshape(T, wl.k).astype(np.float64)
+    shared = G.ex.f64(wl.E) if wl.n_shared else None
+    ref = oracle.moe_layer(xf, ids, g32, G.ex, shared=shared, subset=set(gpu))
+    err = rel_err_rows(y, ref)
+    tol = TOL[wl.wdtype]
+    assert err.max() <= tol, (name, T, err.max())
+    # per-pair expert outputs (fp32, before the bf16 cast): tighter bound
+    o = G.L.o[: (T * wl.k + (T if ws else 0)) * wl.H].cpu().numpy().reshape(-1, wl.H)
+    for t in range(T):
+        for j in range(wl.k):
+            e = int(ids[t, j])
+            if e not in gpu:
+                continue
+            r = oracle.expert_ffn(G.ex.f64(e), xf[t:t + 1])
+            pe = rel_err_rows(o[t * wl.k + j][None, :], r)[0]
+            assert pe <= (1e-5 if wl.wdtype == "f32" else 1.5e-2), (name, t, j, pe)
+    # bitwise run-to-run determinism
+    out2 = G.run(logits, x, gpu, ws)
+    assert torch.equal(out, out2)
+    G.L.close()
+    return err.max()
+
+
+@pytest.mark.parametrize("name,T", [("tiny_fp32", 1), ("tiny_fp32", 8), ("a3b_decode_bf16", 1),
+                                    ("a3b_decode_bf16", 4), ("a3b_decode_bf16", 8), ("v4flash_decode_bf16", 1),
+                                    ("v4flash_decode_bf16", 8), ("v4flash_mxfp4", 1), ("v4flash_mxfp4", 8)])
+@pytest.mark.parametrize("frac", [1.0, 0.5])
+def test_decode_ffn_merge_parity(B, name, T, frac):
+    print(f"[decode] {name} T={T} frac={frac}", flush=True)
+    _decode_case(B, name, T, frac, seed=T * 10 + int(frac * 2))
+
+
+def test_decode_no_gpu_experts_is_host_only(B):
+    """q = 0 and no hits: the GPU part is exactly zero and the output is the host part."""
+    wl = synth.workload("a3b_decode_bf16")
+    G = GpuLayer(B, wl, [0, 1], 2)
+    logits = synth.iid_logits(wl, 2, tag=9)
+    x = synth.activations(wl, 2, tag=9)
+    yh = torch.randn(2 * wl.H, device="cuda")
+    out = G.run(logits, x, [], 0, y_host=yh)
+    want = yh.cpu().numpy().astype(np.float32)
+    got = _out_f64(out, wl, 2).ravel()
+    assert np.abs(got - want).max() <= 2 ** -8 * np.abs(want).max()
+    G.L.close()
+
+
+@pytest.mark.parametrize("name,T", [("a3b_prefill8k_bf16", 40), ("tiny_fp32", 100), ("v4flash_mxfp4", 24)])
+def test_small_prefill_parity(B, name, T):
+    """Ragged prefill-sized batches (T > 8: the grouped path) at sizes the oracle finishes quickly."""
+    print(f"[prefill-small] {name} T={T}", flush=True)
+    wl = synth.workload(name)
+    logits = synth.iid_logits(wl, T, tag=T)
+    ids, _ = oracle.route(logits, wl.k)
+    present = sorted(set(ids.ravel().tolist()))
+    G = GpuLayer(B, wl, present, T)
+    x = synth.activations(wl, T, tag=T)
+    ws = 1 if wl.n_shared else 0
+    out = G.run(logits, x, present, ws)
+    y = _out_f64(out, wl, T)
+    g32 = G.L.w[: T * wl.k].cpu().numpy().reshape(T, wl.k).astype(np.float64)
+    ref = oracle.moe_layer(oracle.act_f64(x, wl.act_dtype), ids, g32, G.ex,
+                           shared=G.ex.f64(wl.E) if ws else None)
+    err = rel_err_rows(y, ref)
+    assert err.max() <= TOL[wl.wdtype], err.max()
+    G.L.close()
