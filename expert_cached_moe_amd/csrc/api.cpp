@@ -216,7 +216,7 @@ int moe_route(moe_ctx* ctx, const float* d_logits, int32_t T, int32_t* d_topk_id
 
 int moe_fill(moe_ctx* ctx, const moe_plan* plan, hipStream_t side) {
     if (!ctx || !plan) return MOE_EINVAL;
-    if (plan->n_fill > 0 && (!ctx->d_slots || !ctx->h_pool || !ctx->fill_event))
+    if (plan->n_fill > 0 && (!ctx->d_slots || !ctx->h_pool))
         return fail(ctx, MOE_ESTATE, "moe_fill needs bound device slots and host pool");
     if (plan->n_fill < 0 || (plan->n_fill > 0 && (!plan->fill || !plan->fill_slot)))
         return fail(ctx, MOE_EINVAL, "bad plan");
