@@ -3,7 +3,8 @@
 
 One step = one pass of the layer's GPU path over one decode batch: router
 softmax + top-k and permutation (moe_route), the SwiGLU experts of the step over
-the expert slots (moe_expert_ffn), and the gate-weighted un-permute and merge
+the expert slots (moe_expert_ffn, token lists from the host copy of the step's
+ids, as the cached pipeline has them), and the gate-weighted un-permute and merge
 (moe_merge_partial).  The K timed steps are captured once in a HIP graph and
 replayed; inputs (logits, activations, expert slots) are resident in HBM before
 the timed region.  The step's expert set comes from the library's own cache
@@ -136,6 +137,7 @@ def main():
 
     # ---------------------------------------------------------------- graph of the timed steps
     stream = torch.cuda.Stream()
+    h_ids_steps = [np.ascontiguousarray(ids_all[t]) for t in range(n_trace)]
 
     def enqueue(s_idx, st, events=None):
         t = s_idx % n_trace
@@ -144,7 +146,7 @@ def main():
         if events is not None:
             events[0].record(st)
         L.ffn(d_x[t * Bt:(t + 1) * Bt], Bt, pools[r], step_experts[t], step_slots[t],
-              shared[r] if shared else None, with_shared, st)
+              shared[r] if shared else None, with_shared, st, h_ids=h_ids_steps[t])
         if events is not None:
             events[1].record(st)
         L.merge(step_experts[t], with_shared, None, Bt, out, st)
@@ -190,7 +192,7 @@ def main():
         pairs = Bt * k + (Bt if with_shared else 0)
         ffn_bytes += (ne + with_shared) * payload_bytes(wl) + Bt * H * (2 if wl.act_dtype == "bf16" else 4) + pairs * H * 4
     achieved = ffn_bytes / n_prof / (ffn_ms / 1e3) / 1e9
-    roofline = {"bound": "hbm", "kernel": "moe_expert_ffn (k_gemv gate/up + k_gemv down)",
+    roofline = {"bound": "hbm", "kernel": "moe_expert_ffn (k_decode_gate_up + k_decode_down)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "ffn_us": round(ffn_ms * 1e3, 2), "bytes_per_launch": round(ffn_bytes / n_prof),
@@ -257,9 +259,10 @@ def pipeline(args, wl, experts, logits, x, dt):
         B.moe_fill(L.ctx, plan, side)
         hits, hslots = plan.get("hit").copy(), plan.get("hit_slot").copy()
         fills, fslots = plan.get("fill").copy(), plan.get("fill_slot").copy()
-        L.ffn(d_x[t * Bt:(t + 1) * Bt], Bt, slots, hits, hslots, shared, ws, main_s)
+        ids_np = h_ids.numpy().reshape(Bt, k)
+        L.ffn(d_x[t * Bt:(t + 1) * Bt], Bt, slots, hits, hslots, shared, ws, main_s, h_ids=ids_np)
         B.moe_fill_wait(L.ctx, main_s)
-        L.ffn(d_x[t * Bt:(t + 1) * Bt], Bt, slots, fills, fslots, None, 0, main_s)
+        L.ffn(d_x[t * Bt:(t + 1) * Bt], Bt, slots, fills, fslots, None, 0, main_s, h_ids=ids_np)
         have_host = plan.c.n_host > 0
         if have_host:
             B.moe_host_ffn(L.ctx, h_x, Bt, h_ids, h_w, plan, h_y, nthreads)

@@ -77,7 +77,7 @@ _sig = {
     "moe_fill": (ctypes.c_int, [vp, _P(moe_plan), vp]),
     "moe_fill_wait": (ctypes.c_int, [vp, vp]),
     "moe_upload": (ctypes.c_int, [vp, vp, vp, ctypes.c_int64, vp]),
-    "moe_expert_ffn": (ctypes.c_int, [vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_int32, vp,
+    "moe_expert_ffn": (ctypes.c_int, [vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp,
                                       ctypes.c_int32, vp, vp, vp]),
     "moe_host_ffn": (ctypes.c_int, [vp, vp, ctypes.c_int32, vp, vp, _P(moe_plan), vp, ctypes.c_int32]),
     "moe_merge_partial": (ctypes.c_int, [vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp,
@@ -256,11 +256,14 @@ def moe_upload(ctx, d_dst, h_src, nbytes, side=None) -> None:
     _check(ctx, _lib.moe_upload(ctx, _ptr(d_dst), _ptr(h_src), nbytes, _stream(side)))
 
 
-def moe_expert_ffn(ctx, d_x, T, d_offsets, d_perm, d_slot_base, h_experts, h_slots, n, d_shared, with_shared,
-                   d_o, d_ws, s=None) -> None:
+def moe_expert_ffn(ctx, d_x, T, h_topk_ids, d_offsets, d_perm, d_slot_base, h_experts, h_slots, n, d_shared,
+                   with_shared, d_o, d_ws, s=None) -> None:
     he = np.ascontiguousarray(h_experts, dtype=np.int32) if h_experts is not None else None
     hs = np.ascontiguousarray(h_slots, dtype=np.int32) if h_slots is not None else None
-    _check(ctx, _lib.moe_expert_ffn(ctx, _ptr(d_x), T, _ptr(d_offsets), _ptr(d_perm), _ptr(d_slot_base),
+    hi = h_topk_ids
+    if isinstance(hi, np.ndarray):
+        hi = np.ascontiguousarray(hi, dtype=np.int32)
+    _check(ctx, _lib.moe_expert_ffn(ctx, _ptr(d_x), T, _ptr(hi), _ptr(d_offsets), _ptr(d_perm), _ptr(d_slot_base),
                                     _ptr(he), _ptr(hs), n, _ptr(d_shared), with_shared, _ptr(d_o), _ptr(d_ws),
                                     _stream(s)))
 

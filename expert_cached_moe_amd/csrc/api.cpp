@@ -68,8 +68,9 @@ WsLayout ws_layout(const moe_config& c, int32_t max_T) {
     const int64_t pairs = T * c.top_k;
     const int64_t chunks = (pairs + kPermChunk - 1) / kPermChunk;
     const int64_t rows = pairs + (c.n_shared ? T : 0);
-    W.hist = 0;
-    W.base = align256(chunks * c.n_experts * 4);
+    W.ctr = 0;
+    W.hist = align256(kCtrBytes);
+    W.base = align256(W.hist + chunks * c.n_experts * 4);
     W.h = align256(W.base + chunks * c.n_experts * 4);
     W.bytes = align256(W.h + rows * int64_t(c.inter) * act_bytes(c));
     return W;
@@ -264,9 +265,9 @@ int moe_fill_wait(moe_ctx* ctx, hipStream_t s) {
     return e == hipSuccess ? MOE_OK : hip_fail(ctx, e, "hipStreamWaitEvent");
 }
 
-int moe_expert_ffn(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* d_offsets, const int32_t* d_perm,
-                   const void* d_slot_base, const int32_t* h_experts, const int32_t* h_slots, int32_t n,
-                   const void* d_shared, int32_t with_shared, float* d_o, void* d_ws, hipStream_t s) {
+int moe_expert_ffn(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* h_topk_ids, const int32_t* d_offsets,
+                   const int32_t* d_perm, const void* d_slot_base, const int32_t* h_experts, const int32_t* h_slots,
+                   int32_t n, const void* d_shared, int32_t with_shared, float* d_o, void* d_ws, hipStream_t s) {
     if (!ctx) return MOE_EINVAL;
     const moe_config& c = ctx->cfg;
     if (T < 0) return fail(ctx, MOE_EINVAL, "T < 0");
@@ -275,20 +276,48 @@ int moe_expert_ffn(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* d_of
     if (with_shared && (!c.n_shared || !d_shared)) return fail(ctx, MOE_EINVAL, "no shared expert");
     if (T == 0 || (n == 0 && !with_shared)) return MOE_OK;
     if (!d_x || !d_o || !d_ws) return fail(ctx, MOE_EINVAL, "null x/o/workspace");
-    if (n > 0 && (!d_offsets || !d_perm || !h_experts || !h_slots || !d_slot_base))
-        return fail(ctx, MOE_EINVAL, "null routed-expert argument");
-    ExpertList list;
-    list.n = 0;
-    std::vector<char> seen(c.n_experts, 0);
+    const bool host_lists = h_topk_ids && T <= kDecodeMaxT && decode_shape_supported(c);
+    if (n > 0 && (!h_experts || !h_slots || !d_slot_base)) return fail(ctx, MOE_EINVAL, "null routed-expert argument");
+    if (n > 0 && !host_lists && (!d_offsets || !d_perm)) return fail(ctx, MOE_EINVAL, "need d_offsets and d_perm");
+    std::vector<int32_t> where(c.n_experts, -1);
     for (int i = 0; i < n; ++i) {
         const int e = h_experts[i], sl = h_slots[i];
-        if (e < 0 || e >= c.n_experts || seen[e]) return fail(ctx, MOE_EINVAL, "expert id out of range or repeated");
+        if (e < 0 || e >= c.n_experts || where[e] >= 0) return fail(ctx, MOE_EINVAL, "expert id out of range or repeated");
         if (sl < 0 || sl >= (1 << 21)) return fail(ctx, MOE_EINVAL, "slot out of range");
-        seen[e] = 1;
-        list.ent[list.n++] = e | (sl << 10);
+        where[e] = i;
     }
-    if (with_shared) list.ent[list.n++] = kSharedTag;
     hipError_t e;
+    if (host_lists) {
+        DecodeList dl;
+        dl.n = n + (with_shared ? 1 : 0);
+        for (int i = 0; i < n; ++i) {
+            dl.ent[i] = h_experts[i] | (h_slots[i] << 10);
+            dl.tokmask[i] = 0;
+            dl.jpack[i] = 0;
+        }
+        for (int t = 0; t < T; ++t)
+            for (int j = 0; j < c.top_k; ++j) {
+                const int id = h_topk_ids[t * c.top_k + j];
+                if (id < 0 || id >= c.n_experts) return fail(ctx, MOE_EINVAL, "top-k id out of range");
+                for (int jj = 0; jj < j; ++jj)
+                    if (h_topk_ids[t * c.top_k + jj] == id) return fail(ctx, MOE_EINVAL, "repeated expert in a token");
+                const int i = where[id];
+                if (i < 0) continue;
+                dl.tokmask[i] |= 1u << t;
+                dl.jpack[i] |= uint32_t(j) << (4 * t);
+            }
+        if (with_shared) {
+            dl.ent[n] = kSharedTag;
+            dl.tokmask[n] = (1u << T) - 1u;
+            dl.jpack[n] = 0;
+        }
+        e = launch_ffn_decode(c, ctx->lay, d_x, T, d_slot_base, d_shared, dl, d_o, d_ws, s);
+        return e == hipSuccess ? MOE_OK : hip_fail(ctx, e, "moe_expert_ffn launch");
+    }
+    ExpertList list;
+    list.n = 0;
+    for (int i = 0; i < n; ++i) list.ent[list.n++] = h_experts[i] | (h_slots[i] << 10);
+    if (with_shared) list.ent[list.n++] = kSharedTag;
     if (T <= kDecodeMaxT || !gemm_shape_supported(c)) {
         if (!gemv_shape_supported(c)) return fail(ctx, MOE_ESHAPE, "no GEMV kernel for this hidden/inter");
         e = launch_ffn_gemv(c, ctx->lay, d_x, T, d_offsets, d_perm, d_slot_base, d_shared, list, d_o, d_ws, s);

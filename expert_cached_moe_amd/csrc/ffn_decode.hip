@@ -1,0 +1,275 @@
+// Decode expert FFN (T <= 8 tokens): batched GEMV over the expert slots (gfx950).
+//
+// Decode reads every weight of every selected expert once per step while only a
+// handful of tokens use it, so the step is bound by HBM bandwidth.  Each lane
+// streams 16-byte chunks of weight rows into registers (consecutive lanes read
+// consecutive chunks: 1 KiB per wave load instruction); the tokens routed to the
+// expert are applied to the registers and each row sum is reduced across the lanes
+// of the row with a halving shuffle exchange.  Every wave is independent (no LDS,
+// no barrier).  Which tokens use which expert comes from the host's copy of the
+// step's top-k ids (the host needs them anyway to plan the cache), packed into the
+// kernel arguments, so these kernels do not wait for the router kernel.
+//
+// Two launches:
+//   gate/up: each wave owns a few intermediate columns (their gate rows and up rows
+//            of the interleaved [2I][H] matrix); after the reduction lanes l and l^32
+//            hold (gate, up) of one column, and h = silu(gate) * up is stored (bf16,
+//            or fp32 for fp32 weights);
+//   down:    rows of [H][I]: o[p][row] = Wd[row] . h[p] in fp32.
+// Expert form: SwiGLU without biases (banandre.com, "The 284B Model on a 32GB GPU
+// Trick", section "Sparsity Is a Lie": experts are small feed-forward networks).
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "ffn_common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+using dev::kWave;
+using namespace ffn;
+
+struct DecodeArgs {
+    const uint8_t* slot_base;
+    const uint8_t* shared_blob;
+    int64_t blob_bytes;
+    int64_t off_w, off_s;  // matrix and MXFP4 scale offsets inside a blob
+    const uint8_t* act;    // gate/up: x [T][H]; down: h [pair rows][I]
+    uint8_t* out;          // gate/up: h; down: o fp32 [pair rows][H]
+    int32_t K, nrows, T, k, I, H;
+    DecodeList list;
+};
+
+// Pair row and activation row of the i-th set bit of the expert's token mask.
+struct TokenIter {
+    uint32_t mask, jpack;
+    bool shared;
+    int T, k;
+    __device__ bool next(int& p, int& t) {
+        if (!mask) return false;
+        t = __builtin_ctz(mask);
+        mask &= mask - 1;
+        p = shared ? T * k + t : t * k + int((jpack >> (4 * t)) & 15u);
+        return true;
+    }
+};
+
+// Rows per wave of the gate/up kernel: small waves keep many loads in flight across
+// the chip (measured on MI355X: one gate+up row pair per wave streams the 50 MB of a
+// 1-token step 20% faster than 8 rows per wave); at least 8 loads per lane.
+template <int CPL> struct GateUpShape {
+    static constexpr int RPW = CPL >= 4 ? 2 : 8 / CPL;  // rows per wave: RPW/2 gate + RPW/2 up
+    static constexpr int WPB = 4;                       // waves per workgroup
+    static constexpr int COLS = RPW / 2 * WPB;          // intermediate columns per workgroup
+};
+
+template <int WT, int CPL>
+__global__ void __launch_bounds__(64 * GateUpShape<CPL>::WPB) k_decode_gate_up(const DecodeArgs a) {
+    constexpr int EPC = Fmt<WT>::EPC;
+    constexpr int AB = Fmt<WT>::ABYTES;
+    constexpr int RPW = GateUpShape<CPL>::RPW, HALF = RPW / 2, WPB = GateUpShape<CPL>::WPB;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int ei = blockIdx.y;
+    const int entry = a.list.ent[ei];
+    const bool shared = (entry & 1023) == kSharedTag;
+    const uint8_t* blob = shared ? a.shared_blob : a.slot_base + int64_t(entry >> 10) * a.blob_bytes;
+    TokenIter it{a.list.tokmask[ei], a.list.jpack[ei], shared, a.T, a.k};
+    const int64_t row_bytes = Fmt<WT>::row_bytes(a.H);
+    const int col0 = (blockIdx.x * WPB + wave) * HALF;       // first intermediate column of the wave
+    // interleaved layout: column i has its gate row at (i/16)*32 + i%16 and its up row 16 further
+    auto row_of = [&](int q) {
+        const int i = col0 + (q < HALF ? q : q - HALF);
+        return (i / 16) * 32 + (i % 16) + (q < HALF ? 0 : 16);
+    };
+    uint4 wv[RPW][CPL];
+    uint8_t sv[RPW][CPL];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+        const int64_t r = row_of(q);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            wv[q][c] = load_w(blob + a.off_w + r * row_bytes, c * kWave + lane);
+            sv[q][c] = WT == WT_FP4 ? blob[a.off_s + r * (a.H / 32) + c * kWave + lane] : uint8_t(0);
+        }
+    }
+    int p, t;
+    while (it.next(p, t)) {
+        float part[RPW];
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) part[q] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            ActChunk<WT> av;
+            load_act<WT>(av, a.act + (int64_t(t) * a.H + int64_t(c * kWave + lane) * EPC) * AB);
+#pragma unroll
+            for (int q = 0; q < RPW; ++q) part[q] = chunk_dot<WT>(wv[q][c], av, sv[q][c], part[q]);
+        }
+        // after the halving reduction lanes l and l^32 hold (gate, up) of one column
+        const int qi = dev::group_reduce_split<RPW, 64>(part, lane);
+        const float up = __shfl_xor(part[0], 32, kWave);
+        if ((lane & 32) == 0 && (lane & (64 / RPW - 1)) == 0)
+            store_h<WT>(a.out, int64_t(p) * a.I + col0 + qi, silu(part[0]) * up);
+    }
+}
+
+// Down rows: LPR lanes per row, CPL chunks per lane, NPASS passes of 64/LPR rows.
+constexpr int kDownPasses = 2, kDownWaves = 8;
+
+template <int WT, int LPR, int CPL>
+__global__ void __launch_bounds__(64 * kDownWaves) k_decode_down(const DecodeArgs a) {
+    constexpr int EPC = Fmt<WT>::EPC;
+    constexpr int AB = Fmt<WT>::ABYTES;
+    constexpr int RPP = kWave / LPR;
+    constexpr int NPASS = kDownPasses;
+    constexpr int RPW = NPASS * RPP;
+    constexpr int RPB = RPW * kDownWaves;
+    static_assert(NPASS <= LPR, "pass layout");
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int g = lane / LPR, lr = lane % LPR;
+    const int ei = blockIdx.y;
+    const int entry = a.list.ent[ei];
+    const bool shared = (entry & 1023) == kSharedTag;
+    const uint8_t* blob = shared ? a.shared_blob : a.slot_base + int64_t(entry >> 10) * a.blob_bytes;
+    TokenIter it{a.list.tokmask[ei], a.list.jpack[ei], shared, a.T, a.k};
+    const int64_t row_bytes = Fmt<WT>::row_bytes(a.I);
+    const int row0 = blockIdx.x * RPB + wave * RPW;
+
+    int p, t;
+    bool have = it.next(p, t);
+    ActChunk<WT> av0[CPL];
+    if (have) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) load_act<WT>(av0[c], a.act + (int64_t(p) * a.I + int64_t(c * LPR + lr) * EPC) * AB);
+    }
+    uint4 wv[NPASS][CPL];
+    uint8_t sv[NPASS][CPL];
+#pragma unroll
+    for (int q = 0; q < NPASS; ++q) {
+        const int r = row0 + q * RPP + g;
+        const bool ok = r < a.nrows;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            wv[q][c] = ok ? load_w(blob + a.off_w + int64_t(r) * row_bytes, c * LPR + lr) : make_uint4(0, 0, 0, 0);
+            sv[q][c] = (WT == WT_FP4 && ok) ? blob[a.off_s + int64_t(r) * (a.I / 32) + c * LPR + lr] : uint8_t(127);
+        }
+    }
+    bool first = true;
+    while (have) {
+        float part[NPASS];
+#pragma unroll
+        for (int q = 0; q < NPASS; ++q) part[q] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            ActChunk<WT> av;
+            if (first)
+                av = av0[c];
+            else
+                load_act<WT>(av, a.act + (int64_t(p) * a.I + int64_t(c * LPR + lr) * EPC) * AB);
+#pragma unroll
+            for (int q = 0; q < NPASS; ++q) part[q] = chunk_dot<WT>(wv[q][c], av, sv[q][c], part[q]);
+        }
+        const int qi = dev::group_reduce_split<NPASS, LPR>(part, lane);
+        const int r = row0 + qi * RPP + g;
+        if ((lr & (LPR / NPASS - 1)) == 0 && r < a.nrows)
+            reinterpret_cast<float*>(a.out)[int64_t(p) * a.H + r] = part[0];
+        first = false;
+        have = it.next(p, t);
+    }
+}
+
+bool pick_down(int d_ch, int* lpr, int* cpl) {
+    for (int l : {64, 32, 16})
+        for (int c : {1, 2, 3, 4, 6, 8})
+            if (l * c == d_ch) { *lpr = l; *cpl = c; return true; }
+    return false;
+}
+
+template <int WT, int CPL>
+hipError_t launch_gu1(const DecodeArgs& a, int n_list, hipStream_t s) {
+    using S = GateUpShape<CPL>;
+    if (a.I % S::COLS) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_decode_gate_up<WT, CPL>), dim3(a.I / S::COLS, n_list), dim3(64 * S::WPB), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int WT>
+hipError_t launch_gu(const DecodeArgs& a, int cpl, int n_list, hipStream_t s) {
+    switch (cpl) {
+        case 1: return launch_gu1<WT, 1>(a, n_list, s);
+        case 2: return launch_gu1<WT, 2>(a, n_list, s);
+        case 4: return launch_gu1<WT, 4>(a, n_list, s);
+        case 8: return launch_gu1<WT, 8>(a, n_list, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int WT>
+hipError_t launch_d(const DecodeArgs& a, int lpr, int cpl, int n_list, hipStream_t s) {
+    const int rpb = kDownPasses * (kWave / lpr) * kDownWaves;
+    const dim3 grid((a.nrows + rpb - 1) / rpb, n_list);
+#define MOE_D(L, C) \
+    if (lpr == L && cpl == C) { \
+        hipLaunchKernelGGL((k_decode_down<WT, L, C>), grid, dim3(64 * kDownWaves), 0, s, a); \
+        return hipGetLastError(); \
+    }
+#define MOE_DL(L) MOE_D(L, 1) MOE_D(L, 2) MOE_D(L, 3) MOE_D(L, 4) MOE_D(L, 6) MOE_D(L, 8)
+    MOE_DL(64) MOE_DL(32) MOE_DL(16)
+#undef MOE_DL
+#undef MOE_D
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool decode_shape_supported(const moe_config& c) {
+    const int gu = ffn::chunks_per_row(c.w_dtype, c.hidden), d = ffn::chunks_per_row(c.w_dtype, c.inter);
+    int l, cc;
+    return c.inter % 16 == 0 && gu % kWave == 0 && (gu / kWave == 1 || gu / kWave == 2 || gu / kWave == 4 ||
+                                                     gu / kWave == 8) && pick_down(d, &l, &cc);
+}
+
+hipError_t launch_ffn_decode(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
+                             const void* slot_base, const void* shared, const DecodeList& list, float* o, void* ws,
+                             hipStream_t s) {
+    const int gu_ch = ffn::chunks_per_row(c.w_dtype, c.hidden), d_ch = ffn::chunks_per_row(c.w_dtype, c.inter);
+    int lpr, cpld;
+    if (!pick_down(d_ch, &lpr, &cpld)) return hipErrorInvalidValue;
+    const WsLayout W = ws_layout(c, T);
+    uint8_t* hbuf = static_cast<uint8_t*>(ws) + W.h;
+    DecodeArgs a;
+    a.slot_base = static_cast<const uint8_t*>(slot_base);
+    a.shared_blob = static_cast<const uint8_t*>(shared);
+    a.blob_bytes = lay.bytes;
+    a.T = T;
+    a.k = c.top_k;
+    a.I = c.inter;
+    a.H = c.hidden;
+    a.list = list;
+    a.off_w = lay.gu;
+    a.off_s = lay.gu_scale;
+    a.act = static_cast<const uint8_t*>(x);
+    a.out = hbuf;
+    a.K = c.hidden;
+    a.nrows = 2 * c.inter;
+    hipError_t e;
+    switch (c.w_dtype) {
+        case MOE_W_F32: e = launch_gu<WT_F32>(a, gu_ch / kWave, list.n, s); break;
+        case MOE_W_BF16: e = launch_gu<WT_BF16>(a, gu_ch / kWave, list.n, s); break;
+        default: e = launch_gu<WT_FP4>(a, gu_ch / kWave, list.n, s); break;
+    }
+    if (e != hipSuccess) return e;
+    a.off_w = lay.d;
+    a.off_s = lay.d_scale;
+    a.act = hbuf;
+    a.out = reinterpret_cast<uint8_t*>(o);
+    a.K = c.inter;
+    a.nrows = c.hidden;
+    switch (c.w_dtype) {
+        case MOE_W_F32: return launch_d<WT_F32>(a, lpr, cpld, list.n, s);
+        case MOE_W_BF16: return launch_d<WT_BF16>(a, lpr, cpld, list.n, s);
+        default: return launch_d<WT_FP4>(a, lpr, cpld, list.n, s);
+    }
+}
+
+}  // namespace moe

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
+#include "ffn_common.h"
 #include "internal.h"
 
 namespace moe {
@@ -25,7 +26,7 @@ namespace {
 
 using dev::kWave;
 
-enum { WT_F32 = 0, WT_BF16 = 1, WT_FP4 = 2 };
+using namespace ffn;
 
 struct GemvArgs {
     const uint8_t* slot_base;
@@ -42,74 +43,6 @@ struct GemvArgs {
     int32_t T, k, I, H;
     ExpertList list;
 };
-
-template <int WT> struct Fmt;
-template <> struct Fmt<WT_F32>  { static constexpr int EPC = 4;  static constexpr int ABYTES = 4; };
-template <> struct Fmt<WT_BF16> { static constexpr int EPC = 8;  static constexpr int ABYTES = 2; };
-template <> struct Fmt<WT_FP4>  { static constexpr int EPC = 32; static constexpr int ABYTES = 2; };
-
-// Activation chunk matching one 16-byte weight chunk.
-template <int WT> struct ActChunk { uint4 v[Fmt<WT>::EPC * Fmt<WT>::ABYTES / 16]; };
-
-template <int WT>
-__device__ __forceinline__ void load_act(ActChunk<WT>& a, const uint8_t* p) {
-    const uint4* q = reinterpret_cast<const uint4*>(p);
-#pragma unroll
-    for (int i = 0; i < int(sizeof(a.v) / 16); ++i) a.v[i] = q[i];
-}
-
-__device__ __forceinline__ float dot2(uint32_t w, uint32_t a, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dev::bf16x2, w), __builtin_bit_cast(dev::bf16x2, a), c,
-                                           false);
-}
-
-// Partial dot product of one weight chunk with one activation chunk.
-template <int WT>
-__device__ __forceinline__ float chunk_dot(const uint4& w, const ActChunk<WT>& a, uint8_t scale, float acc);
-
-template <>
-__device__ __forceinline__ float chunk_dot<WT_F32>(const uint4& w, const ActChunk<WT_F32>& a, uint8_t, float acc) {
-    acc = fmaf(__uint_as_float(w.x), __uint_as_float(a.v[0].x), acc);
-    acc = fmaf(__uint_as_float(w.y), __uint_as_float(a.v[0].y), acc);
-    acc = fmaf(__uint_as_float(w.z), __uint_as_float(a.v[0].z), acc);
-    acc = fmaf(__uint_as_float(w.w), __uint_as_float(a.v[0].w), acc);
-    return acc;
-}
-
-template <>
-__device__ __forceinline__ float chunk_dot<WT_BF16>(const uint4& w, const ActChunk<WT_BF16>& a, uint8_t, float acc) {
-    acc = dot2(w.x, a.v[0].x, acc);
-    acc = dot2(w.y, a.v[0].y, acc);
-    acc = dot2(w.z, a.v[0].z, acc);
-    acc = dot2(w.w, a.v[0].w, acc);
-    return acc;
-}
-
-// MXFP4: 32 e2m1 elements of one scale block.  The unscaled products are summed in
-// fp32 and the block sum is multiplied by the power-of-two scale 2^(s-127).
-template <>
-__device__ __forceinline__ float chunk_dot<WT_FP4>(const uint4& w, const ActChunk<WT_FP4>& a, uint8_t s, float acc) {
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-    float part = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint4 av = a.v[q];  // 8 bf16 activations: elements 8q .. 8q+7
-        const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
-        // byte b of the word holds elements 2b (low nibble) and 2b + 1 (high nibble)
-        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ww[q], 1.0f, 0),
-                                               __builtin_bit_cast(dev::bf16x2, aw[0]), part, false);
-        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ww[q], 1.0f, 1),
-                                               __builtin_bit_cast(dev::bf16x2, aw[1]), part, false);
-        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ww[q], 1.0f, 2),
-                                               __builtin_bit_cast(dev::bf16x2, aw[2]), part, false);
-        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ww[q], 1.0f, 3),
-                                               __builtin_bit_cast(dev::bf16x2, aw[3]), part, false);
-    }
-    const float sc = s ? __uint_as_float(uint32_t(s) << 23) : __uint_as_float(0x00400000u);
-    return fmaf(part, sc, acc);
-}
-
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 constexpr int kMaxBatch = 8;  // tokens buffered between workgroup barriers (gate/up)
 
@@ -220,8 +153,6 @@ k_gemv(const GemvArgs a) {
 struct Variant {
     int lpr, cpl;
 };
-
-int chunks_per_row(int wt, int K) { return wt == WT_F32 ? K / 4 : wt == WT_BF16 ? K / 8 : K / 32; }
 
 bool pick(int nch, Variant* v) {
     static const int lprs[3] = {64, 32, 16};

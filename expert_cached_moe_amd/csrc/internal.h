@@ -39,9 +39,12 @@ BlobLayout blob_layout(const moe_config& c);
 inline int act_bytes(const moe_config& c) { return c.w_dtype == MOE_W_F32 ? 4 : 2; }
 
 // Scratch layout inside the caller's workspace.
+// The counter block sits at offset 0 (same address for every T): it must be zero
+// before the first call and every call leaves it zeroed.
 struct WsLayout {
-    int64_t hist = 0, base = 0, h = 0, bytes = 0;
+    int64_t ctr = 0, hist = 0, base = 0, h = 0, bytes = 0;
 };
+constexpr int64_t kCtrBytes = 4 * (2 + kMaxExperts + 1 + 61);  // ticket, finished, per-entry counts
 WsLayout ws_layout(const moe_config& c, int32_t max_T);
 
 // A small persistent worker pool for the host FFN.
@@ -99,6 +102,22 @@ struct ExpertList {
     int32_t ent[kMaxExperts + 1];  // expert | slot << 10; expert == kSharedTag: shared
 };
 
+// Decode (T <= kDecodeMaxT) expert list with per-expert token sets from the host's
+// top-k ids: token t uses the expert when bit t of tokmask is set, as pair
+// t*k + ((jpack >> 4t) & 15).  The shared expert uses every token.
+constexpr int kMaxDecodeList = kDecodeMaxT * kMaxTopK + 1;
+struct DecodeList {
+    int32_t n;
+    int32_t ent[kMaxDecodeList];      // expert | slot << 10; kSharedTag: shared expert
+    uint32_t tokmask[kMaxDecodeList];
+    uint32_t jpack[kMaxDecodeList];
+};
+
+hipError_t launch_ffn_decode(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
+                             const void* slot_base, const void* shared, const DecodeList& list, float* o, void* ws,
+                             hipStream_t s);
+bool decode_shape_supported(const moe_config& c);
+
 hipError_t launch_route(const moe_config& c, const float* logits, int32_t T, int32_t* ids, float* w,
                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
                         hipStream_t s);
@@ -109,6 +128,7 @@ hipError_t launch_ffn_gemv(const moe_config& c, const BlobLayout& lay, const voi
                            const void* shared, const ExpertList& list, float* o, void* ws,
                            hipStream_t s);
 bool gemv_shape_supported(const moe_config& c);
+
 
 hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
                            const int32_t* offsets, const int32_t* perm, const void* slot_base,

@@ -28,26 +28,43 @@ __global__ void __launch_bounds__(256) k_merge(const MergeArgs a) {
     const int t = blockIdx.y;
     const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= a.H) return;
+    // every partial row of the token is loaded at once (rows of CPU experts hold stale
+    // values and are dropped by a select, never multiplied), next to the ids and gates
+    float4 v[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+        v[j] = (a.o && j < a.k) ? *reinterpret_cast<const float4*>(a.o + (int64_t(t) * a.k + j) * a.H + c)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    float g[kMaxTopK];
+    int64_t row[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+        row[j] = -1;
+        g[j] = 0.0f;
+        if (j < a.k) {
+            const int p = t * a.k + j;
+            const int e = a.ids[p];
+            if ((a.mask[e >> 5] >> (e & 31)) & 1u) {
+                row[j] = p;
+                g[j] = a.w[p];
+            }
+        }
+    }
+    float4 sh = make_float4(0.f, 0.f, 0.f, 0.f), yh = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.with_shared) sh = *reinterpret_cast<const float4*>(a.o + (int64_t(a.T) * a.k + t) * a.H + c);
+    if (a.y_host) yh = *reinterpret_cast<const float4*>(a.y_host + int64_t(t) * a.H + c);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < a.k; ++j) {
-        const int p = t * a.k + j;
-        const int e = a.ids[p];
-        if (!((a.mask[e >> 5] >> (e & 31)) & 1u)) continue;
-        const float g = a.w[p];
-        const float4 v = *reinterpret_cast<const float4*>(a.o + int64_t(p) * a.H + c);
-        acc.x = fmaf(g, v.x, acc.x);
-        acc.y = fmaf(g, v.y, acc.y);
-        acc.z = fmaf(g, v.z, acc.z);
-        acc.w = fmaf(g, v.w, acc.w);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+        if (row[j] >= 0) {
+            acc.x = fmaf(g[j], v[j].x, acc.x);
+            acc.y = fmaf(g[j], v[j].y, acc.y);
+            acc.z = fmaf(g[j], v[j].z, acc.z);
+            acc.w = fmaf(g[j], v[j].w, acc.w);
+        }
     }
-    if (a.with_shared) {
-        const float4 v = *reinterpret_cast<const float4*>(a.o + (int64_t(a.T) * a.k + t) * a.H + c);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-    if (a.y_host) {
-        const float4 v = *reinterpret_cast<const float4*>(a.y_host + int64_t(t) * a.H + c);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
+    acc.x += sh.x; acc.y += sh.y; acc.z += sh.z; acc.w += sh.w;
+    acc.x += yh.x; acc.y += yh.y; acc.z += yh.z; acc.w += yh.w;
     if (a.out_bf16) {
         uint2 r;
         r.x = dev::pack_bf16x2(acc.x, acc.y);

@@ -27,6 +27,40 @@ constexpr int kRouteWaves = 16;              // tokens per workgroup in the larg
 constexpr int kBlock = kRouteWaves * kWave;  // 1024 threads
 static_assert(kBlock == kPermChunk, "one pair per thread per permutation chunk");
 
+// (value, id) arg-max step: take the other candidate if it ranks first
+// (larger logit, or equal logit and lower id).  Empty candidates are (-inf, INT_MAX).
+__device__ __forceinline__ void take_better(float& v, int& e, float ov, int oe) {
+    if (ov > v || (ov == v && oe < e)) {
+        v = ov;
+        e = oe;
+    }
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_step(float& v, int& e) {
+    const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+    const int oe = __builtin_amdgcn_mov_dpp(e, CTRL, 0xF, 0xF, false);
+    take_better(v, e, ov, oe);
+}
+
+// Wave-wide arg-max: butterflies inside each row of 16 lanes with DPP (quad swaps,
+// then rotations by 4 and 8), then the four row winners through readlane.  The
+// result is uniform across the wave.
+__device__ __forceinline__ void wave_argmax(float& v, int& e) {
+    dpp_step<0xB1>(v, e);   // quad_perm [1,0,3,2]
+    dpp_step<0x4E>(v, e);   // quad_perm [2,3,0,1]
+    dpp_step<0x124>(v, e);  // row_ror:4
+    dpp_step<0x128>(v, e);  // row_ror:8
+    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    int be = __builtin_amdgcn_readlane(e, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r)
+        take_better(bv, be, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r)),
+                    __builtin_amdgcn_readlane(e, 16 * r));
+    v = bv;
+    e = be;
+}
+
 // Route one token with one wave.  EPL = experts per lane (ceil(E/64)).
 template <int EPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ lrow, int E, int k, int renorm,
@@ -45,19 +79,12 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lrow, int 
     float my_v = 0.0f, v0 = 0.0f;
     int my_e = -1;
     for (int j = 0; j < k; ++j) {
-        float bv = 0.0f;
+        float bv = -INFINITY;
         int be = INT_MAX;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int e = lane + kWave * i;
-            if (live[i] && (be == INT_MAX || v[i] > bv)) { bv = v[i]; be = e; }
-        }
-#pragma unroll
-        for (int d = kWave / 2; d >= 1; d >>= 1) {
-            const float ov = __shfl_xor(bv, d, kWave);
-            const int oe = __shfl_xor(be, d, kWave);
-            if (oe != INT_MAX && (be == INT_MAX || ov > bv || (ov == bv && oe < be))) { bv = ov; be = oe; }
-        }
+        for (int i = 0; i < EPL; ++i)
+            if (live[i]) take_better(bv, be, v[i], lane + kWave * i);
+        wave_argmax(bv, be);
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
             if (lane + kWave * i == be) live[i] = false;
@@ -66,17 +93,18 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lrow, int 
     }
     // softmax over the selected logits (or over all E), shifted by the largest logit
     const float ex = lane < k ? expf(my_v - v0) : 0.0f;
-    float den;
+    float den = 0.0f;
     if (renorm) {
-        den = ex;
+        for (int j = 0; j < k; ++j) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
     } else {
-        den = 0.0f;
+        float s = 0.0f;
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
-            if (lane + kWave * i < E) den += expf(v[i] - v0);
-    }
+            if (lane + kWave * i < E) s += expf(v[i] - v0);
 #pragma unroll
-    for (int d = kWave / 2; d >= 1; d >>= 1) den += __shfl_xor(den, d, kWave);
+        for (int d = kWave / 2; d >= 1; d >>= 1) s += __shfl_xor(s, d, kWave);
+        den = s;
+    }
     if (lane < k) {
         ids_out[lane] = my_e;
         w_out[lane] = ex / den;
@@ -209,6 +237,54 @@ __global__ __launch_bounds__(kBlock) void k_route_small(const float* __restrict_
     for (int p0 = 0; p0 < n; p0 += kBlock) scatter_chunk(s_ids + p0, p0, n - p0, E, s_run, s_wc, perm, inv);
 }
 
+// T*k <= 64 (decode): route, then the whole grouping by wave 0 with ballots.  For the
+// pair of lane p with expert e: eq = lanes with expert e, lt = lanes with a smaller
+// expert (bit-serial compare of the 10-bit ids, most significant bit first), so
+// its position is |lt| + |eq below p|.
+__global__ __launch_bounds__(256) void k_route_tiny(const float* __restrict__ logits, int T, int E, int k,
+                                                    int renorm, int32_t* __restrict__ ids, float* __restrict__ w,
+                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    __shared__ int32_t s_ids[kWave];
+    const int tid = threadIdx.x;
+    route_dispatch(logits, T, E, k, renorm, 0, 4, ids, w, s_ids);
+    __syncthreads();
+    const int n = T * k;
+    for (int e = tid; e < E; e += 256) {
+        int c = 0, lt = 0;
+        for (int p = 0; p < n; ++p) {
+            const int v = s_ids[p];
+            c += v == e;
+            lt += v < e;
+        }
+        counts[e] = c;
+        offsets[e] = lt;
+    }
+    if (tid == 0) offsets[E] = n;
+    if (tid < kWave) {
+        const bool valid = tid < n;
+        const int e = valid ? s_ids[tid] : 0;
+        uint64_t eq = __ballot(valid), lt = 0;
+#pragma unroll
+        for (int b = 9; b >= 0; --b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t b1 = __ballot(valid && bit);
+            if (bit) {
+                lt |= eq & ~b1;
+                eq &= b1;
+            } else {
+                eq &= ~b1;
+            }
+        }
+        const uint64_t below = tid == 0 ? 0ull : (~0ull >> (kWave - tid));
+        if (valid) {
+            const int pos = __popcll(lt) + __popcll(eq & below);
+            perm[pos] = tid;
+            inv[tid] = pos;
+        }
+    }
+}
+
 // Large T: one wave per token.
 __global__ __launch_bounds__(kBlock) void k_route(const float* __restrict__ logits, int T, int E, int k, int renorm,
                                                   int32_t* __restrict__ ids, float* __restrict__ w) {
@@ -270,6 +346,11 @@ hipError_t launch_route(const moe_config& c, const float* logits, int32_t T, int
                         hipStream_t s) {
     const int E = c.n_experts, k = c.top_k;
     const int64_t n = int64_t(T) * k;
+    if (n <= kWave) {
+        hipLaunchKernelGGL(k_route_tiny, dim3(1), dim3(256), 0, s, logits, T, E, k, c.renormalize, ids, w, counts,
+                           offsets, perm, inv);
+        return hipGetLastError();
+    }
     if (n <= kSmallRouteMaxPairs) {
         hipLaunchKernelGGL(k_route_small, dim3(1), dim3(kBlock), 0, s, logits, T, E, k, c.renormalize, ids, w,
                            counts, offsets, perm, inv);

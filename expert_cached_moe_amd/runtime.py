@@ -20,7 +20,7 @@ class LayerBuffers:
         self.max_T = max_T
         self.blob_bytes = B.moe_expert_bytes(cfg)
         dev = torch.device(device)
-        self.ws = torch.empty(B.moe_workspace_bytes(cfg, max_T), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(B.moe_workspace_bytes(cfg, max_T), dtype=torch.uint8, device=dev)  # counters start at 0
         n = max(1, max_T * self.k)
         self.ids = torch.empty(n, dtype=torch.int32, device=dev)
         self.w = torch.empty(n, dtype=torch.float32, device=dev)
@@ -45,9 +45,11 @@ class LayerBuffers:
         B.moe_route(self.ctx, logits, T, self.ids, self.w, self.counts, self.offsets, self.perm, self.inv,
                     self.ws, stream)
 
-    def ffn(self, x, T, slot_base, experts, slots, shared=None, with_shared=0, stream=None):
+    def ffn(self, x, T, slot_base, experts, slots, shared=None, with_shared=0, stream=None, h_ids=None):
+        """h_ids: host copy of the step's top-k ids (decode: the kernels then skip the router's
+        device outputs); None: the token lists come from this buffer set's last route."""
         n = len(experts)
-        B.moe_expert_ffn(self.ctx, x, T, self.offsets, self.perm, slot_base, experts, slots, n, shared,
+        B.moe_expert_ffn(self.ctx, x, T, h_ids, self.offsets, self.perm, slot_base, experts, slots, n, shared,
                          with_shared, self.o, self.ws, stream)
 
     def merge(self, gpu_experts, with_shared, y_host, T, out, stream=None):

@@ -129,7 +129,10 @@ const char* moe_status_string(int status);
  * in the host pool and in the device slots, so a fill is one contiguous copy
  * ([B] "Elastic Memory": experts are read into their final host layout). */
 int64_t moe_expert_bytes(const moe_config* cfg);
-/* Device scratch bytes needed by moe_route + moe_expert_ffn for up to max_T tokens. */
+/* Device scratch bytes needed by moe_route + moe_expert_ffn for up to max_T tokens.
+ * The workspace must be zero-filled once before its first use; every call leaves
+ * its first kilobytes (queue counters of the decode FFN) zeroed again, the rest is
+ * scratch.  Calls that share a workspace must be ordered (one stream, or events). */
 int64_t moe_workspace_bytes(const moe_config* cfg, int32_t max_T);
 /* Rows of the pair-output buffer d_o for T tokens: T*k (+ T with a shared expert). */
 int64_t moe_pair_rows(const moe_config* cfg, int32_t T);
@@ -202,16 +205,19 @@ int moe_upload(moe_ctx* ctx, void* d_dst, const void* h_src, int64_t bytes, hipS
  *   expert e = topk_ids[t][j] is listed in h_experts, read from the blob at
  *   d_slot_base + h_slots[i]*moe_expert_bytes; with with_shared = 1 also
  *   o[T*k + t] for the shared expert blob d_shared (all tokens).
- *   d_x [T][H] activations; d_offsets, d_perm from moe_route; h_experts /
- *   h_slots: host arrays of n (<= E) distinct expert ids and slot indices;
- *   d_o [moe_pair_rows][H] fp32 (rows of unlisted experts are not written);
- *   d_ws: moe_workspace_bytes(max_T >= T).
+ *   d_x [T][H] activations; h_experts / h_slots: host arrays of n (<= E) distinct
+ *   expert ids and slot indices; d_o [moe_pair_rows][H] fp32 (rows of unlisted
+ *   experts are not written); d_ws: moe_workspace_bytes(max_T >= T).
+ *   Which tokens use an expert comes from h_topk_ids (host copy [T][k] of the
+ *   step's ids, as moe_lru_step consumes) when given and T <= 8; the kernels then
+ *   do not read d_offsets / d_perm and need not wait for moe_route.  Otherwise
+ *   d_offsets / d_perm from moe_route are read on the device.
  * T <= 8 runs the decode path (HBM-bound batched GEMV); larger T runs the
  * grouped GEMM on MFMA.  Errors: MOE_EINVAL (ids, null), MOE_ESHAPE. */
-int moe_expert_ffn(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* d_offsets,
-                   const int32_t* d_perm, const void* d_slot_base, const int32_t* h_experts,
-                   const int32_t* h_slots, int32_t n, const void* d_shared, int32_t with_shared,
-                   float* d_o, void* d_ws, hipStream_t s);
+int moe_expert_ffn(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* h_topk_ids,
+                   const int32_t* d_offsets, const int32_t* d_perm, const void* d_slot_base,
+                   const int32_t* h_experts, const int32_t* h_slots, int32_t n, const void* d_shared,
+                   int32_t with_shared, float* d_o, void* d_ws, hipStream_t s);
 
 /* CPU SwiGLU experts of the plan's host set from the bound host pool:
  * h_y[t] = sum over j with topk_ids[t][j] in plan->host of w[t][j]*FFN(x_t),

@@ -127,20 +127,23 @@ class GpuLayer:
         if wl.n_shared:
             self.shared = pack_pool(self.cfg, [self.ex.raw(wl.E)], pin=False).cuda()
 
-    def run(self, logits, x, gpu_experts, with_shared, y_host=None):
+    def run(self, logits, x, gpu_experts, with_shared, y_host=None, host_ids=True):
+        """host_ids: decode token lists from the host copy of the ids (else from the router's
+        device offsets/permutation)."""
         T = logits.shape[0]
         wl, L = self.wl, self.L
         L.route(torch.from_numpy(np.ascontiguousarray(logits)).cuda(), T)
+        h_ids = L.ids[: T * wl.k].cpu().numpy().reshape(T, wl.k) if host_ids else None
         dx = _dev_act(x)
         slots = [self.slot[e] for e in gpu_experts]
-        L.ffn(dx, T, self.pool, gpu_experts, slots, self.shared, with_shared)
+        L.ffn(dx, T, self.pool, gpu_experts, slots, self.shared, with_shared, h_ids=h_ids)
         out = torch.empty(T * wl.H, dtype=torch.float32 if wl.act_dtype == "f32" else torch.int16, device="cuda")
         L.merge(gpu_experts, with_shared, y_host, T, out)
         torch.cuda.synchronize()
         return out
 
 
-def _decode_case(B, name, T, frac, seed):
+def _decode_case(B, name, T, frac, seed, host_ids=True):
     wl = synth.workload(name)
     lg, _ = synth.zipf_reuse_trace(wl, T, 3, tag=seed)
     logits = lg[2]
@@ -153,7 +156,7 @@ def _decode_case(B, name, T, frac, seed):
     G = GpuLayer(B, wl, pool_order, T)
     x = synth.activations(wl, T, tag=seed)
     ws = 1 if wl.n_shared else 0
-    out = G.run(logits, x, gpu, ws)
+    out = G.run(logits, x, gpu, ws, host_ids=host_ids)
     y = _out_f64(out, wl, T)
     xf = oracle.act_f64(x, wl.act_dtype)
     g32 = G.L.w[: T * wl.k].cpu().numpy().reshape(T, wl.k).astype(np.float64)
@@ -173,7 +176,7 @@ def _decode_case(B, name, T, frac, seed):
             pe = rel_err_rows(o[t * wl.k + j][None, :], r)[0]
             assert pe <= (1e-5 if wl.wdtype == "f32" else 1.5e-2), (name, t, j, pe)
     # bitwise run-to-run determinism
-    out2 = G.run(logits, x, gpu, ws)
+    out2 = G.run(logits, x, gpu, ws, host_ids=host_ids)
     assert torch.equal(out, out2)
     G.L.close()
     return err.max()
@@ -186,6 +189,13 @@ def _decode_case(B, name, T, frac, seed):
 def test_decode_ffn_merge_parity(B, name, T, frac):
     print(f"[decode] {name} T={T} frac={frac}", flush=True)
     _decode_case(B, name, T, frac, seed=T * 10 + int(frac * 2))
+
+
+@pytest.mark.parametrize("name,T", [("tiny_fp32", 3), ("a3b_decode_bf16", 8), ("v4flash_mxfp4", 2)])
+def test_decode_device_lists_parity(B, name, T):
+    """Decode with the token lists taken from the router's device outputs."""
+    print(f"[decode-device-lists] {name} T={T}", flush=True)
+    _decode_case(B, name, T, 0.75, seed=T + 100, host_ids=False)
 
 
 def test_decode_no_gpu_experts_is_host_only(B):
