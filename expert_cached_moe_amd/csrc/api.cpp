@@ -71,7 +71,8 @@ WsLayout ws_layout(const moe_config& c, int32_t max_T) {
     W.ctr = 0;
     W.hist = align256(kCtrBytes);
     W.base = align256(W.hist + chunks * c.n_experts * 4);
-    W.h = align256(W.base + chunks * c.n_experts * 4);
+    W.tiles = align256(W.base + chunks * c.n_experts * 4);
+    W.h = align256(W.tiles + gemm_tile_ints(c, int32_t(T)) * 4);
     W.bytes = align256(W.h + rows * int64_t(c.inter) * act_bytes(c));
     return W;
 }

@@ -1,17 +1,353 @@
 // Prefill expert FFN (T > 8 tokens): grouped GEMM on MFMA (gfx950).
+//
+// Prefill routes thousands of tokens to nearly every expert (banandre.com, "The
+// 284B Model on a 32GB GPU Trick", section "The Three Failure Modes of Existing
+// Engines"), so each expert's work is a dense product over the rows routed to it.
+// Pairs are grouped by expert (moe_route's stable permutation); per expert
+//   GEMM 1:  G = A_e . Wgu^T  (A_e = x rows of the expert's pairs, gathered)
+//            epilogue h = silu(gate) * up, stored as bf16 at the pair's sorted row;
+//   GEMM 2:  O = h_e . Wd^T, fp32, stored at the pair's row p = perm[pos].
+// bf16 inputs, fp32 accumulation on v_mfma_f32_16x16x32_bf16; MXFP4 weights are
+// dequantised to bf16 (exactly) while their tile is staged into LDS.
+//
+// Tiling: a workgroup computes a 128 x 128 output tile in K steps of 64 with four
+// waves of 64 x 64 (4 x 4 MFMA tiles).  Global tiles for step s+1 are loaded into
+// registers while step s is computed from LDS (rows padded by 16 bytes).  Gate
+// and up rows are interleaved in blocks of 16 in the weight layout, so the gate
+// and up MFMA tiles of one column land in the same lanes and the SwiGLU epilogue
+// needs no data exchange.  Tiles are numbered expert-major and each of the 8 XCDs
+// takes a contiguous range, so the A rows and weights of one expert are re-read
+// from that XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
+#include "ffn_common.h"
 #include "internal.h"
 
 namespace moe {
+namespace {
 
-bool gemm_shape_supported(const moe_config&) { return false; }
+using dev::kWave;
 
-hipError_t launch_ffn_gemm(const moe_config&, const BlobLayout&, const void*, int32_t, const int32_t*,
-                           const int32_t*, const void*, const void*, const ExpertList&, float*, void*,
-                           hipStream_t) {
-    return hipErrorInvalidValue;
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int kThreads = 256;
+constexpr int LDS_STRIDE = BK + 8;   // bf16 elements per LDS row (16-byte pad)
+constexpr int kXcds = 8;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+
+struct TileMapArgs {
+    const int32_t* offsets;
+    int32_t T, n_shared_tiles;
+    int32_t* tiles;   // [0]: count, then (entry << 16) | m_tile
+    ExpertList list;
+};
+
+// Tiles of every listed expert in list order: ceil(rows / BM) m-tiles each.
+__global__ void __launch_bounds__(1024) k_tile_map(const TileMapArgs a) {
+    __shared__ int32_t s_cnt[kMaxExperts + 1];
+    __shared__ int32_t s_base[kMaxExperts + 2];
+    const int tid = threadIdx.x;
+    const int n = a.list.n;
+    for (int i = tid; i < n; i += blockDim.x) {
+        const int e = a.list.ent[i] & 1023;
+        const int rows = e == kSharedTag ? a.T : a.offsets[e + 1] - a.offsets[e];
+        s_cnt[i] = (rows + BM - 1) / BM;
+    }
+    __syncthreads();
+    if (tid < kWave) {                        // exclusive scan, 9 entries per lane
+        constexpr int kPer = (kMaxExperts + 1 + kWave - 1) / kWave;
+        int loc[kPer], sum = 0;
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int i = tid * kPer + q;
+            loc[q] = i < n ? s_cnt[i] : 0;
+            sum += loc[q];
+        }
+        int incl = sum;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int v = __shfl_up(incl, d, kWave);
+            if (tid >= d) incl += v;
+        }
+        int run = incl - sum;
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int i = tid * kPer + q;
+            if (i < n) s_base[i] = run;
+            run += loc[q];
+        }
+        if (tid == kWave - 1) {
+            s_base[n] = run;
+            a.tiles[0] = run;
+        }
+    }
+    __syncthreads();
+    for (int i = 0; i < n; ++i) {
+        const int cnt = s_base[i + 1] - s_base[i];
+        for (int m = tid; m < cnt; m += blockDim.x) a.tiles[1 + s_base[i] + m] = (i << 16) | m;
+    }
+}
+
+struct GemmArgs {
+    const uint8_t* slot_base;
+    const uint8_t* shared_blob;
+    int64_t blob_bytes;
+    int64_t off_w, off_s;      // weight matrix (and MXFP4 scales) inside a blob
+    const uint8_t* a_src;      // GEMM 1: x [T][H] bf16; GEMM 2: h [rows][I] bf16
+    void* out;                 // GEMM 1: h bf16 [rows][I]; GEMM 2: o fp32 [pair rows][H]
+    const int32_t* offsets;
+    const int32_t* perm;
+    const int32_t* tiles;
+    int32_t T, k, K, N;        // K: reduction length, N: output columns of the matrix
+    int32_t I, H;
+    int32_t grid;              // launched workgroups (a multiple of the XCD count)
+    ExpertList list;
+};
+
+// MXFP4 -> bf16 of 32 elements (16 code bytes) with the block scale folded in.
+__device__ __forceinline__ void fp4_to_bf16(const uint4 codes, uint8_t s, uint4 out[4]) {
+    const float sc = s ? __uint_as_float(uint32_t(s) << 23) : __uint_as_float(0x00400000u);
+    const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const dev::bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 0);
+        const dev::bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 1);
+        const dev::bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 2);
+        const dev::bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 3);
+        out[q] = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                            __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+    }
+}
+
+// MODE 0: gate/up GEMM with SwiGLU epilogue; MODE 1: down GEMM.  FP4: MXFP4 weights.
+template <int MODE, bool FP4>
+__global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDS_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDS_STRIDE];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // XCD-contiguous logical tile id (workgroups are dealt round-robin to the XCDs)
+    const int b = blockIdx.x;
+    const int per_xcd = a.grid / kXcds;
+    const int lid = (b % kXcds) * per_xcd + b / kXcds;
+    const int n_tiles = a.N / BN;
+    const int slot = lid / n_tiles, nt = lid % n_tiles;
+    if (slot >= a.tiles[0]) return;
+    const int tinfo = a.tiles[1 + slot];
+    const int ei = tinfo >> 16, mt = tinfo & 0xFFFF;
+    const int entry = a.list.ent[ei];
+    const int e = entry & 1023;
+    const bool shared = e == kSharedTag;
+    const uint8_t* blob = shared ? a.shared_blob : a.slot_base + int64_t(entry >> 10) * a.blob_bytes;
+    const int base = shared ? 0 : a.offsets[e];
+    const int rows = shared ? a.T : a.offsets[e + 1] - base;
+    const int m0 = mt * BM, n0 = nt * BN;
+
+    // ---- this thread's 4 A chunks and 4 B chunks per K step: row = c / 8, 16-byte column c % 8
+    const uint8_t* arow[4];
+    bool avalid[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = tid + kThreads * i;
+        const int r = c / 8;
+        avalid[i] = m0 + r < rows;
+        int64_t src_row = 0;
+        if (avalid[i]) {
+            if (MODE == 0)
+                src_row = shared ? (m0 + r) : a.perm[base + m0 + r] / a.k;        // token of the pair
+            else
+                src_row = shared ? int64_t(a.T) * a.k + m0 + r : base + m0 + r;  // h row
+        }
+        arow[i] = a.a_src + src_row * int64_t(a.K) * 2;
+    }
+    const int64_t wrow_bytes = FP4 ? a.K / 2 : int64_t(a.K) * 2;
+
+    uint4 ra[4], rb[4];
+    uint4 rbq;                // MXFP4: one 16-byte code chunk (32 elements, one scale) per thread
+    uint8_t rbs;
+    auto load_tiles = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + kThreads * i;
+            ra[i] = avalid[i] ? *reinterpret_cast<const uint4*>(arow[i] + (int64_t(k0) + (c % 8) * 8) * 2)
+                              : make_uint4(0, 0, 0, 0);
+        }
+        if (!FP4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = tid + kThreads * i;
+                const int r = c / 8;
+                rb[i] = ffn::load_w(blob + a.off_w + int64_t(n0 + r) * wrow_bytes + int64_t(k0) * 2, c % 8);
+            }
+        } else {
+            // 128 rows x 64 K = 128 rows x 2 chunks of 16 code bytes: one chunk per thread
+            const int r = tid >> 1, half = tid & 1;
+            rbq = *reinterpret_cast<const uint4*>(blob + a.off_w + int64_t(n0 + r) * wrow_bytes + k0 / 2 + half * 16);
+            rbs = blob[a.off_s + int64_t(n0 + r) * (a.K / 32) + k0 / 32 + half];
+        }
+    };
+    auto store_tiles = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + kThreads * i;
+            *reinterpret_cast<uint4*>(&As[(c / 8) * LDS_STRIDE + (c % 8) * 8]) = ra[i];
+        }
+        if (!FP4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = tid + kThreads * i;
+                *reinterpret_cast<uint4*>(&Bs[(c / 8) * LDS_STRIDE + (c % 8) * 8]) = rb[i];
+            }
+        } else {
+            const int r = tid >> 1, half = tid & 1;
+            uint4 v[4];
+            fp4_to_bf16(rbq, rbs, v);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&Bs[r * LDS_STRIDE + half * 32 + q * 8]) = v[q];
+        }
+    };
+
+    typedef __attribute__((ext_vector_type(4))) float f32x4;
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = a.K / BK;
+    load_tiles(0);
+    for (int ks = 0; ks < nk; ++ks) {
+        __syncthreads();                 // previous step's LDS reads are done
+        store_tiles();
+        __syncthreads();
+        if (ks + 1 < nk) load_tiles((ks + 1) * BK);
+#pragma unroll
+        for (int kk = 0; kk < BK / 32; ++kk) {
+            bf16x8 af[4], bfr[4];
+            const int kc = kk * 32 + (lane / 16) * 8;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                af[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * 64 + i * 16 + lane % 16) * LDS_STRIDE + kc]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * 64 + j * 16 + lane % 16) * LDS_STRIDE + kc]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+    }
+
+    // ---- epilogue: lane holds column lane%16 and rows (lane/16)*4 .. +4 of each 16x16 tile
+    if (MODE == 0) {
+        uint16_t* h = static_cast<uint16_t*>(a.out);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int col = (n0 + wn * 64 + jj * 32) / 32 * 16 + lane % 16;   // intermediate column
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = m0 + wm * 64 + i * 16 + (lane / 16) * 4 + r;
+                    if (row < rows) {
+                        const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
+                        const int64_t hrow = shared ? int64_t(a.T) * a.k + row : base + row;
+                        h[hrow * a.I + col] = dev::f32_to_bf16_bits(ffn::silu(g) * u);
+                    }
+                }
+            }
+        }
+    } else {
+        float* o = static_cast<float*>(a.out);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + wm * 64 + i * 16 + (lane / 16) * 4 + r;
+                if (row < rows) {
+                    const int64_t p = shared ? int64_t(a.T) * a.k + row : a.perm[base + row];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) o[p * a.H + n0 + wn * 64 + j * 16 + lane % 16] = acc[i][j][r];
+                }
+            }
+        }
+    }
+}
+
+int max_tiles(const moe_config& c, int32_t T) {
+    const int64_t pairs = int64_t(T) * c.top_k;
+    return int((pairs + BM - 1) / BM + c.n_experts + 1 + (T + BM - 1) / BM + 1);
+}
+
+}  // namespace
+
+int64_t gemm_tile_ints(const moe_config& c, int32_t T) { return 1 + max_tiles(c, T); }
+
+bool gemm_shape_supported(const moe_config& c) {
+    if (c.w_dtype == MOE_W_F32) return false;
+    return c.hidden % BK == 0 && c.inter % BK == 0 && (2 * c.inter) % BN == 0 && c.hidden % BN == 0 &&
+           c.hidden >= BK && c.inter >= BK;
+}
+
+hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
+                           const int32_t* offsets, const int32_t* perm, const void* slot_base,
+                           const void* shared, const ExpertList& list, float* o, void* ws, hipStream_t s) {
+    const WsLayout W = ws_layout(c, T);
+    int32_t* tiles = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + W.tiles);
+    TileMapArgs tm;
+    tm.offsets = offsets;
+    tm.T = T;
+    tm.n_shared_tiles = 0;
+    tm.tiles = tiles;
+    tm.list = list;
+    hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, s, tm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    const int mt = max_tiles(c, T);
+    const bool fp4 = c.w_dtype == MOE_W_MXFP4;
+    GemmArgs a;
+    a.slot_base = static_cast<const uint8_t*>(slot_base);
+    a.shared_blob = static_cast<const uint8_t*>(shared);
+    a.blob_bytes = lay.bytes;
+    a.offsets = offsets;
+    a.perm = perm;
+    a.tiles = tiles;
+    a.T = T;
+    a.k = c.top_k;
+    a.I = c.inter;
+    a.H = c.hidden;
+    a.list = list;
+    uint8_t* hbuf = static_cast<uint8_t*>(ws) + W.h;
+    // GEMM 1: [rows x H] . [2I x H]^T -> h [rows x I]
+    a.off_w = lay.gu;
+    a.off_s = lay.gu_scale;
+    a.a_src = static_cast<const uint8_t*>(x);
+    a.out = hbuf;
+    a.K = c.hidden;
+    a.N = 2 * c.inter;
+    a.grid = (mt * (a.N / BN) + kXcds - 1) / kXcds * kXcds;
+    if (fp4)
+        hipLaunchKernelGGL((k_gemm<0, true>), dim3(a.grid), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_gemm<0, false>), dim3(a.grid), dim3(kThreads), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // GEMM 2: h [rows x I] . [H x I]^T -> o [pair rows x H]
+    a.off_w = lay.d;
+    a.off_s = lay.d_scale;
+    a.a_src = hbuf;
+    a.out = o;
+    a.K = c.inter;
+    a.N = c.hidden;
+    a.grid = (mt * (a.N / BN) + kXcds - 1) / kXcds * kXcds;
+    if (fp4)
+        hipLaunchKernelGGL((k_gemm<1, true>), dim3(a.grid), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_gemm<1, false>), dim3(a.grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace moe

@@ -42,8 +42,9 @@ inline int act_bytes(const moe_config& c) { return c.w_dtype == MOE_W_F32 ? 4 : 
 // The counter block sits at offset 0 (same address for every T): it must be zero
 // before the first call and every call leaves it zeroed.
 struct WsLayout {
-    int64_t ctr = 0, hist = 0, base = 0, h = 0, bytes = 0;
+    int64_t ctr = 0, hist = 0, base = 0, tiles = 0, h = 0, bytes = 0;
 };
+int64_t gemm_tile_ints(const moe_config& c, int32_t T);  // tile-list entries of the grouped GEMM
 constexpr int64_t kCtrBytes = 4 * (2 + kMaxExperts + 1 + 61);  // ticket, finished, per-entry counts
 WsLayout ws_layout(const moe_config& c, int32_t max_T);
 

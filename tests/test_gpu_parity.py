@@ -231,3 +231,32 @@ def test_small_prefill_parity(B, name, T):
     err = rel_err_rows(y, ref)
     assert err.max() <= TOL[wl.wdtype], err.max()
     G.L.close()
+
+
+@pytest.mark.parametrize("name,n_sample", [("a3b_prefill8k_bf16", 24), ("v4flash_mxfp4", 8)])
+def test_prefill_full_size_sampled(B, name, n_sample):
+    """8192-token prefill chunk at full size through the grouped GEMM; the oracle checks a
+    sample of tokens (first, last and random ones) one by one."""
+    print(f"[prefill-full] {name}", flush=True)
+    wl = synth.workload(name)
+    T = wl.T
+    ex = Experts(wl)
+    logits = synth.iid_logits(wl, T)
+    G = GpuLayer(B, wl, list(range(wl.E)), T, ex=ex)
+    x = synth.activations(wl, T, tag=3)
+    ws = 1 if wl.n_shared else 0
+    out = G.run(logits, x, list(range(wl.E)), ws)
+    y = _out_f64(out, wl, T)
+    ids = G.L.ids[: T * wl.k].cpu().numpy().reshape(T, wl.k)
+    rids, _ = oracle.route(logits, wl.k)
+    assert np.array_equal(ids, rids)
+    g32 = G.L.w[: T * wl.k].cpu().numpy().reshape(T, wl.k).astype(np.float64)
+    rng = np.random.default_rng(0)
+    sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_sample - 2, replace=False)]))
+    xs = oracle.act_f64(x[sample], wl.act_dtype)
+    conv = lambda e: oracle.expert_f64(ex.raw(e), wl.wdtype)          # no fp64 cache: bounded memory
+    ref = oracle.moe_layer(xs, rids[sample], g32[sample], conv, shared=conv(wl.E) if ws else None)
+    err = rel_err_rows(y[sample], ref)
+    assert err.max() <= TOL[wl.wdtype], err.max()
+    assert np.median(err) <= 4e-3, np.median(err)       # typical error of bf16 h rounding, well under the bound
+    G.L.close()
