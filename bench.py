@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pipeline", action="store_true")
     ap.add_argument("--pipeline-steps", type=int, default=400)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-reps", type=int, default=20)
     return ap.parse_args()
 
 
@@ -209,6 +211,12 @@ def main():
                          "gpu_experts_per_step": round(mean_distinct, 3), "step": "route+permute+ffn+merge, HIP graph"},
               "roofline": roofline}
 
+    # ---------------------------------------------------------------- 8K prefill chunks (context)
+    if not args.no_prefill:
+        del pools
+        torch.cuda.empty_cache()
+        result["prefill"] = {name: prefill(args, name) for name in ("a3b_prefill8k_bf16", "v4flash_mxfp4")}
+
     # ---------------------------------------------------------------- full cached pipeline (context)
     if not args.no_pipeline:
         result["pipeline"] = pipeline(args, wl, experts, logits, x, dt)
@@ -218,6 +226,76 @@ def main():
         result["cpu_baseline"] = cpu_baseline(args, wl, experts, logits, x)
     B.moe_destroy(planner)
     print(json.dumps(result), flush=True)
+
+
+def prefill(args, name):
+    """One 8192-token chunk through route + grouped GEMMs + merge with the layer's pool
+    resident in HBM, captured in a graph and replayed; MFMA roofline of the two GEMMs."""
+    import torch
+    import synth
+    from expert_cached_moe_amd import binding as B
+    from expert_cached_moe_amd.runtime import LayerBuffers, pack_pool
+    wl = synth.workload(name)
+    T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
+    dt = {"f32": B.MOE_W_F32, "bf16": B.MOE_W_BF16, "mxfp4": B.MOE_W_MXFP4}[wl.wdtype]
+    cfg = B.make_config(H, I, E, k, wl.n_shared, 0, 1, dt)
+    experts = synth.expert_weights_many(wl, range(E + wl.n_shared), threads=16)
+    pool = pack_pool(cfg, [experts[e] for e in range(E)], pin=False).cuda()
+    shared = pack_pool(cfg, [experts[E]], pin=False).cuda() if wl.n_shared else None
+    del experts
+    L = LayerBuffers(cfg, T)
+    d_logits = torch.from_numpy(synth.iid_logits(wl, T)).cuda()
+    x = synth.activations(wl, T, tag=3)
+    d_x = torch.from_numpy(x.view(np.int16)).cuda()
+    out = torch.empty(T * H, dtype=torch.int16, device="cuda")
+    allx = np.arange(E, dtype=np.int32)
+    ws = 1 if wl.n_shared else 0
+    stream = torch.cuda.Stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def step(events=False):
+        L.route(d_logits, T, stream)
+        if events:
+            ev[0].record(stream)
+        L.ffn(d_x, T, pool, allx, allx, shared, ws, stream)
+        if events:
+            ev[1].record(stream)
+        L.merge(allx, ws, None, T, out, stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(args.prefill_reps):
+            step()
+    with torch.cuda.stream(stream):
+        g.replay()
+        torch.cuda.synchronize()
+        ev[2].record(stream)
+        g.replay()
+        ev[3].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[2].elapsed_time(ev[3]) / args.prefill_reps
+    # FFN alone (events around the grouped GEMMs of eager chunks)
+    gemm_ms = []
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            step(events=True)
+            torch.cuda.synchronize()
+            gemm_ms.append(ev[0].elapsed_time(ev[1]))
+    gms = float(np.median(gemm_ms))
+    flops = 6.0 * T * k * H * I + (6.0 * T * H * I if wl.n_shared else 0.0)
+    tflops = flops / (gms / 1e3) / 1e12
+    nb = B.moe_expert_bytes(cfg)
+    del g
+    L.close()
+    return {"tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_chunk": round(ms, 4), "tokens": T,
+            "gemm_ms": round(gms, 4), "gemm_tflops": round(tflops, 1),
+            "mfma_frac_bf16_peak": round(tflops / 2500.0, 4), "gflop": round(flops / 1e9, 1),
+            "pool_gb": round(nb * E / 1e9, 3), "weights": wl.wdtype,
+            "note": "layer pool resident in HBM; MXFP4 weights dequantised to bf16 MFMA inputs"}
 
 
 def pipeline(args, wl, experts, logits, x, dt):

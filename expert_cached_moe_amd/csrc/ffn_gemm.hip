@@ -83,10 +83,8 @@ __global__ void __launch_bounds__(1024) k_tile_map(const TileMapArgs a) {
         }
     }
     __syncthreads();
-    for (int i = 0; i < n; ++i) {
-        const int cnt = s_base[i + 1] - s_base[i];
-        for (int m = tid; m < cnt; m += blockDim.x) a.tiles[1 + s_base[i] + m] = (i << 16) | m;
-    }
+    for (int i = tid; i < n; i += blockDim.x)
+        for (int m = 0; m < s_cnt[i]; ++m) a.tiles[1 + s_base[i] + m] = (i << 16) | m;
 }
 
 struct GemmArgs {

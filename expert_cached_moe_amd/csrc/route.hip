@@ -305,26 +305,43 @@ __global__ __launch_bounds__(kBlock) void k_perm_hist(const int32_t* __restrict_
 }
 
 // counts, offsets, and base[chunk][e] = offsets[e] + pairs of e in earlier chunks.
+// Thread e walks its column of hist eight chunks at a time (independent loads in
+// flight), then the experts' totals are scanned.
 __global__ __launch_bounds__(kBlock) void k_perm_scan(const int32_t* __restrict__ hist, int nchunks, int E,
                                                       int32_t* __restrict__ base, int32_t* __restrict__ counts,
                                                       int32_t* __restrict__ offsets) {
     __shared__ int32_t s_cnt[kMaxExperts];
     __shared__ int32_t s_off[kMaxExperts + 1];
+    constexpr int U = 8;
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += kBlock) {
         int run = 0;
-        for (int c = 0; c < nchunks; ++c) {
-            const int h = hist[int64_t(c) * E + e];
-            base[int64_t(c) * E + e] = run;
-            run += h;
+        for (int c0 = 0; c0 < nchunks; c0 += U) {
+            int h[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) h[u] = c0 + u < nchunks ? hist[int64_t(c0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (c0 + u < nchunks) base[int64_t(c0 + u) * E + e] = run;
+                run += h[u];
+            }
         }
         s_cnt[e] = run;
     }
     __syncthreads();
     wave0_scan(s_cnt, E, s_off, offsets, counts);
     __syncthreads();
-    for (int e = tid; e < E; e += kBlock)
-        for (int c = 0; c < nchunks; ++c) base[int64_t(c) * E + e] += s_off[e];
+    for (int e = tid; e < E; e += kBlock) {
+        const int off = s_off[e];
+        for (int c0 = 0; c0 < nchunks; c0 += U) {
+            int b[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) b[u] = c0 + u < nchunks ? base[int64_t(c0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (c0 + u < nchunks) base[int64_t(c0 + u) * E + e] = b[u] + off;
+        }
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void k_perm_scatter(const int32_t* __restrict__ ids, int n, int E,
