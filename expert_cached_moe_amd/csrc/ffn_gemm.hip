@@ -10,12 +10,12 @@
 // bf16 inputs, fp32 accumulation on v_mfma_f32_16x16x32_bf16; MXFP4 weights are
 // dequantised to bf16 (exactly) while their tile is staged into LDS.
 //
-// Tiling: a workgroup computes a 128 x 128 output tile in K steps of 64 with four
-// waves of 64 x 64 (4 x 4 MFMA tiles).  Global tiles for step s+1 are loaded into
-// registers while step s is computed from LDS (rows padded by 16 bytes).  Gate
-// and up rows are interleaved in blocks of 16 in the weight layout, so the gate
-// and up MFMA tiles of one column land in the same lanes and the SwiGLU epilogue
-// needs no data exchange.  Tiles are numbered expert-major and each of the 8 XCDs
+// Tiling: a workgroup computes a BM x BN output tile in K steps of 64; its waves
+// each own a block of MFMA tiles (16x16x32 or 32x32x16), fed from LDS rows padded by
+// 16 bytes, with the next step's global tiles prefetched into registers.  Gate and
+// up rows are interleaved in blocks of 16 in the weight layout, so the gate and up
+// values of a column meet in the same lane (16-wide tiles) or one lane exchange away
+// (32-wide tiles) and the SwiGLU epilogue stays in registers.  Tiles are numbered expert-major and each of the 8 XCDs
 // takes a contiguous range, so the A rows and weights of one expert are re-read
 // from that XCD's L2.
 #include <hip/hip_runtime.h>
@@ -29,12 +29,40 @@ namespace {
 
 using dev::kWave;
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int kThreads = 256;
-constexpr int LDS_STRIDE = BK + 8;   // bf16 elements per LDS row (16-byte pad)
+// Tile configuration (chosen by measurement on MI355X; see the kernel comment).
+#ifndef MOE_GEMM_BM
+#define MOE_GEMM_BM 128
+#define MOE_GEMM_BN 256
+#define MOE_GEMM_WM 2
+#define MOE_GEMM_WN 4
+#define MOE_GEMM_MF 32
+#define MOE_GEMM_DB 0
+#endif
+constexpr int BM = MOE_GEMM_BM, BN = MOE_GEMM_BN, BK = 64;
+constexpr int WM = MOE_GEMM_WM, WN = MOE_GEMM_WN;   // wave grid
+constexpr int MF = MOE_GEMM_MF;                     // MFMA tile: 16 (16x16x32) or 32 (32x32x16)
+constexpr bool DB = MOE_GEMM_DB;                    // two LDS stages, one barrier per K step
+constexpr int KMF = MF == 16 ? 32 : 16;             // K per MFMA
+constexpr int NACC = MF == 16 ? 4 : 16;             // accumulator floats per lane per tile
+constexpr int kThreads = WM * WN * 64;
+constexpr int TM = BM / WM, TN = BN / WN;           // wave tile
+constexpr int FM = TM / MF, FN = TN / MF;           // MFMA tiles per wave
+constexpr int ACH = BM * 8 / kThreads;              // 16-byte A chunks per thread per K step
+constexpr int BCH = BN * 8 / kThreads;
+constexpr int FCH = BN * 2 / kThreads > 0 ? BN * 2 / kThreads : 1;  // MXFP4 code chunks per thread
+constexpr int LDS_STRIDE = BK + 8;                  // bf16 elements per LDS row (16-byte pad)
+constexpr int kStages = DB ? 2 : 1;
+constexpr int kLdsBytes = kStages * (BM + BN) * LDS_STRIDE * 2;
 constexpr int kXcds = 8;
+static_assert(ACH * kThreads == BM * 8 && BCH * kThreads == BN * 8, "chunking");
+static_assert(FM * MF == TM && FN * MF == TN, "wave tile");
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+template <int M> struct AccT;
+template <> struct AccT<16> { typedef f32x4 T; };
+template <> struct AccT<32> { typedef f32x16 T; };
 
 struct TileMapArgs {
     const int32_t* offsets;
@@ -118,13 +146,23 @@ __device__ __forceinline__ void fp4_to_bf16(const uint4 codes, uint8_t s, uint4 
     }
 }
 
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // MODE 0: gate/up GEMM with SwiGLU epilogue; MODE 1: down GEMM.  FP4: MXFP4 weights.
+// WM x WN waves, each TM x TN = FM x FN MFMA tiles.  The next K step's global tiles
+// are loaded into registers while the current LDS stage is consumed.
 template <int MODE, bool FP4>
 __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDS_STRIDE];
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    uint16_t* As = lds;                                 // [stages][BM][LDS_STRIDE]
+    uint16_t* Bs = lds + kStages * BM * LDS_STRIDE;     // [stages][BN][LDS_STRIDE]
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
 
     // XCD-contiguous logical tile id (workgroups are dealt round-robin to the XCDs)
     const int b = blockIdx.x;
@@ -142,12 +180,13 @@ __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
     const int base = shared ? 0 : a.offsets[e];
     const int rows = shared ? a.T : a.offsets[e + 1] - base;
     const int m0 = mt * BM, n0 = nt * BN;
+    const int K = a.K;
 
-    // ---- this thread's 4 A chunks and 4 B chunks per K step: row = c / 8, 16-byte column c % 8
-    const uint8_t* arow[4];
-    bool avalid[4];
+    // ---- per K step each thread moves ACH chunks of A and BCH of B (row = c / 8, 16-byte column c % 8)
+    const uint8_t* arow[ACH];
+    bool avalid[ACH];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < ACH; ++i) {
         const int c = tid + kThreads * i;
         const int r = c / 8;
         avalid[i] = m0 + r < rows;
@@ -158,121 +197,182 @@ __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
             else
                 src_row = shared ? int64_t(a.T) * a.k + m0 + r : base + m0 + r;  // h row
         }
-        arow[i] = a.a_src + src_row * int64_t(a.K) * 2;
+        arow[i] = a.a_src + src_row * int64_t(K) * 2 + (c % 8) * 16;
     }
-    const int64_t wrow_bytes = FP4 ? a.K / 2 : int64_t(a.K) * 2;
+    const int64_t wrow_bytes = FP4 ? K / 2 : int64_t(K) * 2;
+    const uint8_t* wbase = blob + a.off_w;
+    const uint8_t* sbase = blob + a.off_s;
 
-    uint4 ra[4], rb[4];
-    uint4 rbq;                // MXFP4: one 16-byte code chunk (32 elements, one scale) per thread
-    uint8_t rbs;
-    auto load_tiles = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + kThreads * i;
-            ra[i] = avalid[i] ? *reinterpret_cast<const uint4*>(arow[i] + (int64_t(k0) + (c % 8) * 8) * 2)
-                              : make_uint4(0, 0, 0, 0);
-        }
-        if (!FP4) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = tid + kThreads * i;
-                const int r = c / 8;
-                rb[i] = ffn::load_w(blob + a.off_w + int64_t(n0 + r) * wrow_bytes + int64_t(k0) * 2, c % 8);
-            }
-        } else {
-            // 128 rows x 64 K = 128 rows x 2 chunks of 16 code bytes: one chunk per thread
-            const int r = tid >> 1, half = tid & 1;
-            rbq = *reinterpret_cast<const uint4*>(blob + a.off_w + int64_t(n0 + r) * wrow_bytes + k0 / 2 + half * 16);
-            rbs = blob[a.off_s + int64_t(n0 + r) * (a.K / 32) + k0 / 32 + half];
-        }
-    };
-    auto store_tiles = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + kThreads * i;
-            *reinterpret_cast<uint4*>(&As[(c / 8) * LDS_STRIDE + (c % 8) * 8]) = ra[i];
-        }
-        if (!FP4) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int c = tid + kThreads * i;
-                *reinterpret_cast<uint4*>(&Bs[(c / 8) * LDS_STRIDE + (c % 8) * 8]) = rb[i];
-            }
-        } else {
-            const int r = tid >> 1, half = tid & 1;
-            uint4 v[4];
-            fp4_to_bf16(rbq, rbs, v);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) *reinterpret_cast<uint4*>(&Bs[r * LDS_STRIDE + half * 32 + q * 8]) = v[q];
-        }
-    };
+    uint4 ra[ACH], rb[BCH];
+    uint4 rbq[FCH];
+    uint8_t rbs[FCH];
 
-    typedef __attribute__((ext_vector_type(4))) float f32x4;
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#define MOE_GEMM_LOAD(k0)                                                                                    \
+    {                                                                                                        \
+        _Pragma("unroll") for (int i = 0; i < ACH; ++i) ra[i] =                                              \
+            avalid[i] ? *reinterpret_cast<const uint4*>(arow[i] + int64_t(k0) * 2) : make_uint4(0, 0, 0, 0); \
+        if (!FP4) {                                                                                          \
+            _Pragma("unroll") for (int i = 0; i < BCH; ++i) {                                                \
+                const int c = tid + kThreads * i;                                                            \
+                rb[i] = ffn::load_w(wbase + int64_t(n0 + c / 8) * wrow_bytes + int64_t(k0) * 2, c % 8);      \
+            }                                                                                                \
+        } else {                                                                                             \
+            _Pragma("unroll") for (int i = 0; i < FCH; ++i) {                                                \
+                const int c = tid + kThreads * i, r = c >> 1, half = c & 1;                                  \
+                if (c < BN * 2) {                                                                            \
+                    rbq[i] = *reinterpret_cast<const uint4*>(wbase + int64_t(n0 + r) * wrow_bytes + (k0) / 2 + half * 16); \
+                    rbs[i] = sbase[int64_t(n0 + r) * (K / 32) + (k0) / 32 + half];                           \
+                }                                                                                            \
+            }                                                                                                \
+        }                                                                                                    \
+    }
+#define MOE_GEMM_STORE(st)                                                                                   \
+    {                                                                                                        \
+        uint16_t* as_ = As + (st) * BM * LDS_STRIDE;                                                         \
+        uint16_t* bs_ = Bs + (st) * BN * LDS_STRIDE;                                                         \
+        _Pragma("unroll") for (int i = 0; i < ACH; ++i) {                                                    \
+            const int c = tid + kThreads * i;                                                                \
+            *reinterpret_cast<uint4*>(&as_[(c / 8) * LDS_STRIDE + (c % 8) * 8]) = ra[i];                     \
+        }                                                                                                    \
+        if (!FP4) {                                                                                          \
+            _Pragma("unroll") for (int i = 0; i < BCH; ++i) {                                                \
+                const int c = tid + kThreads * i;                                                            \
+                *reinterpret_cast<uint4*>(&bs_[(c / 8) * LDS_STRIDE + (c % 8) * 8]) = rb[i];                 \
+            }                                                                                                \
+        } else {                                                                                             \
+            _Pragma("unroll") for (int i = 0; i < FCH; ++i) {                                                \
+                const int c = tid + kThreads * i, r = c >> 1, half = c & 1;                                  \
+                if (c < BN * 2) {                                                                            \
+                    uint4 v[4];                                                                              \
+                    fp4_to_bf16(rbq[i], rbs[i], v);                                                          \
+                    _Pragma("unroll") for (int q = 0; q < 4; ++q)                                            \
+                        *reinterpret_cast<uint4*>(&bs_[r * LDS_STRIDE + half * 32 + q * 8]) = v[q];          \
+                }                                                                                            \
+            }                                                                                                \
+        }                                                                                                    \
+    }
 
-    const int nk = a.K / BK;
-    load_tiles(0);
-    for (int ks = 0; ks < nk; ++ks) {
-        __syncthreads();                 // previous step's LDS reads are done
-        store_tiles();
+    typename AccT<MF>::T acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < NACC; ++q) acc[i][j][q] = 0.0f;
+
+#define MOE_GEMM_COMPUTE(st)                                                                                 \
+    {                                                                                                        \
+        const uint16_t* as_ = As + (st) * BM * LDS_STRIDE;                                                   \
+        const uint16_t* bs_ = Bs + (st) * BN * LDS_STRIDE;                                                   \
+        _Pragma("unroll") for (int kk = 0; kk < BK / KMF; ++kk) {                                            \
+            bf16x8 af[FM], bfr[FN];                                                                          \
+            const int kc = kk * KMF + (lane / MF) * 8;                                                       \
+            _Pragma("unroll") for (int i = 0; i < FM; ++i) af[i] =                                           \
+                *reinterpret_cast<const bf16x8*>(&as_[(wm * TM + i * MF + lane % MF) * LDS_STRIDE + kc]);    \
+            _Pragma("unroll") for (int j = 0; j < FN; ++j) bfr[j] =                                          \
+                *reinterpret_cast<const bf16x8*>(&bs_[(wn * TN + j * MF + lane % MF) * LDS_STRIDE + kc]);    \
+            _Pragma("unroll") for (int i = 0; i < FM; ++i) _Pragma("unroll") for (int j = 0; j < FN; ++j)    \
+                acc[i][j] = mfma(af[i], bfr[j], acc[i][j]);                                                  \
+        }                                                                                                    \
+    }
+
+    const int nk = K / BK;
+    if (DB) {
+        MOE_GEMM_LOAD(0)
+        MOE_GEMM_STORE(0)
         __syncthreads();
-        if (ks + 1 < nk) load_tiles((ks + 1) * BK);
-#pragma unroll
-        for (int kk = 0; kk < BK / 32; ++kk) {
-            bf16x8 af[4], bfr[4];
-            const int kc = kk * 32 + (lane / 16) * 8;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * 64 + i * 16 + lane % 16) * LDS_STRIDE + kc]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * 64 + j * 16 + lane % 16) * LDS_STRIDE + kc]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int ks = 0; ks < nk; ++ks) {
+            const int st = ks & 1;
+            if (ks + 1 < nk) MOE_GEMM_LOAD((ks + 1) * BK)
+            MOE_GEMM_COMPUTE(st)
+            if (ks + 1 < nk) MOE_GEMM_STORE(st ^ 1)
+            __syncthreads();
+        }
+    } else {
+        MOE_GEMM_LOAD(0)
+        for (int ks = 0; ks < nk; ++ks) {
+            __syncthreads();                 // previous step's LDS reads are done
+            MOE_GEMM_STORE(0)
+            __syncthreads();
+            if (ks + 1 < nk) MOE_GEMM_LOAD((ks + 1) * BK)
+            MOE_GEMM_COMPUTE(0)
         }
     }
+#undef MOE_GEMM_COMPUTE
+#undef MOE_GEMM_LOAD
+#undef MOE_GEMM_STORE
 
-    // ---- epilogue: lane holds column lane%16 and rows (lane/16)*4 .. +4 of each 16x16 tile
+    // ---- epilogue.  MF = 16: lane holds column lane%16, value q at row (lane/16)*4 + q.
+    //      MF = 32: lane holds column lane%32, value q at row 8*(q/4) + (lane/32)*4 + q%4.
+    auto row_of = [&](int i, int q) {
+        return MF == 16 ? m0 + wm * TM + i * 16 + (lane / 16) * 4 + q
+                        : m0 + wm * TM + i * 32 + 8 * (q / 4) + (lane / 32) * 4 + (q % 4);
+    };
     if (MODE == 0) {
+        // gate/up interleave of 16: a 16-wide tile pair (MF=16) or one 32-wide tile (MF=32)
+        // holds the gate and up values of 16 intermediate columns
         uint16_t* h = static_cast<uint16_t*>(a.out);
+        if (MF == 16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+            for (int jj = 0; jj < FN / 2; ++jj) {
+                const int col = (n0 + wn * TN + jj * 32) / 32 * 16 + lane % 16;
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int col = (n0 + wn * 64 + jj * 32) / 32 * 16 + lane % 16;   // intermediate column
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = m0 + wm * 64 + i * 16 + (lane / 16) * 4 + r;
-                    if (row < rows) {
-                        const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
-                        const int64_t hrow = shared ? int64_t(a.T) * a.k + row : base + row;
-                        h[hrow * a.I + col] = dev::f32_to_bf16_bits(ffn::silu(g) * u);
+                    for (int q = 0; q < NACC; ++q) {
+                        const int row = row_of(i, q);
+                        if (row < rows) {
+                            const int64_t hrow = shared ? int64_t(a.T) * a.k + row : base + row;
+                            h[hrow * a.I + col] = dev::f32_to_bf16_bits(ffn::silu(acc[i][2 * jj][q]) * acc[i][2 * jj + 1][q]);
+                        }
                     }
-                }
+            }
+        } else {
+            const bool gate_lane = (lane % 32) < 16;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int col = (n0 + wn * TN + j * 32) / 32 * 16 + lane % 16;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int q = 0; q < NACC; ++q) {
+                        const float up = __shfl_xor(acc[i][j][q], 16, kWave);
+                        const int row = row_of(i, q);
+                        if (gate_lane && row < rows) {
+                            const int64_t hrow = shared ? int64_t(a.T) * a.k + row : base + row;
+                            h[hrow * a.I + col] = dev::f32_to_bf16_bits(ffn::silu(acc[i][j][q]) * up);
+                        }
+                    }
             }
         }
     } else {
         float* o = static_cast<float*>(a.out);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm * 64 + i * 16 + (lane / 16) * 4 + r;
+            for (int q = 0; q < NACC; ++q) {
+                const int row = row_of(i, q);
                 if (row < rows) {
                     const int64_t p = shared ? int64_t(a.T) * a.k + row : a.perm[base + row];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) o[p * a.H + n0 + wn * 64 + j * 16 + lane % 16] = acc[i][j][r];
+                    for (int j = 0; j < FN; ++j) o[p * a.H + n0 + wn * TN + j * MF + lane % MF] = acc[i][j][q];
                 }
             }
-        }
     }
+}
+
+// The GEMM stages use more than the default 64 KiB of LDS per workgroup.
+hipError_t allow_lds() {
+    static hipError_t once = [] {
+        const void* ks[4] = {reinterpret_cast<const void*>(&k_gemm<0, false>), reinterpret_cast<const void*>(&k_gemm<0, true>),
+                             reinterpret_cast<const void*>(&k_gemm<1, false>), reinterpret_cast<const void*>(&k_gemm<1, true>)};
+        for (const void* k : ks) {
+            hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }();
+    return once;
 }
 
 int max_tiles(const moe_config& c, int32_t T) {
@@ -328,10 +428,11 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     a.K = c.hidden;
     a.N = 2 * c.inter;
     a.grid = (mt * (a.N / BN) + kXcds - 1) / kXcds * kXcds;
+    if ((e = allow_lds()) != hipSuccess) return e;
     if (fp4)
-        hipLaunchKernelGGL((k_gemm<0, true>), dim3(a.grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((k_gemm<0, true>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
     else
-        hipLaunchKernelGGL((k_gemm<0, false>), dim3(a.grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((k_gemm<0, false>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // GEMM 2: h [rows x I] . [H x I]^T -> o [pair rows x H]
     a.off_w = lay.d;
@@ -342,9 +443,9 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     a.N = c.hidden;
     a.grid = (mt * (a.N / BN) + kXcds - 1) / kXcds * kXcds;
     if (fp4)
-        hipLaunchKernelGGL((k_gemm<1, true>), dim3(a.grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((k_gemm<1, true>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
     else
-        hipLaunchKernelGGL((k_gemm<1, false>), dim3(a.grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((k_gemm<1, false>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
     return hipGetLastError();
 }
 
