@@ -32,10 +32,20 @@ using dev::kWave;
 // Tile configuration (chosen by measurement on MI355X; see the kernel comment).
 #ifndef MOE_GEMM_BM
 #define MOE_GEMM_BM 128
+#endif
+#ifndef MOE_GEMM_BN
 #define MOE_GEMM_BN 256
+#endif
+#ifndef MOE_GEMM_WM
 #define MOE_GEMM_WM 2
+#endif
+#ifndef MOE_GEMM_WN
 #define MOE_GEMM_WN 4
+#endif
+#ifndef MOE_GEMM_MF
 #define MOE_GEMM_MF 32
+#endif
+#ifndef MOE_GEMM_DB
 #define MOE_GEMM_DB 0
 #endif
 constexpr int BM = MOE_GEMM_BM, BN = MOE_GEMM_BN, BK = 64;
@@ -361,6 +371,188 @@ __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- pipelined bf16 GEMM
+// Direct global->LDS loads (global_load_lds_dwordx4: lane i of a wave writes 16
+// bytes at the wave's LDS base + 16 i) into a ring of NSTAGE stages of BK = 32, so
+// the loads run NSTAGE - 1 steps ahead of the MFMAs and need no staging registers.
+// LDS rows are 64 bytes (4 chunks of 8 bf16); chunk c of row r is stored at slot
+// c ^ ((r >> 2) & 3), which keeps the 16 lanes of a fragment read on distinct banks.
+// A rows past the expert's end load row 0 of the expert (their outputs are dropped).
+#ifndef MOE_GEMM_DMA
+#define MOE_GEMM_DMA 1
+#endif
+#ifndef MOE_DMA_BM
+#define MOE_DMA_BM MOE_GEMM_BM
+#endif
+#ifndef MOE_DMA_BN
+#define MOE_DMA_BN 256
+#endif
+#ifndef MOE_DMA_STAGES
+#define MOE_DMA_STAGES 3
+#endif
+#ifndef MOE_DMA_NMAJOR
+#define MOE_DMA_NMAJOR 0
+#endif
+namespace dma {
+constexpr int BM = MOE_DMA_BM, BN = MOE_DMA_BN, WM = 2, WN = 4, MF = 32, BK = 32, NSTAGE = MOE_DMA_STAGES;
+constexpr int kThreads = WM * WN * 64, NW = WM * WN;
+constexpr int TM = BM / WM, TN = BN / WN, FM = TM / MF, FN = TN / MF;
+constexpr int ROWB = BK * 2;                              // bytes per LDS row
+constexpr int STAGE_BYTES = (BM + BN) * ROWB;
+constexpr int Q = (BM + BN) * ROWB / 1024 / NW;           // 1 KiB load instructions per wave per stage
+constexpr int kLdsBytes = NSTAGE * STAGE_BYTES;
+static_assert(Q * NW * 1024 == STAGE_BYTES, "stage split");
+static_assert(BM == ::moe::BM, "the tile list is built with the same row-tile height for every GEMM kernel");
+static_assert((BM * ROWB) % 1024 == 0, "A/B boundary on a load block");
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    // s_waitcnt with vmcnt = N (bits 3:0 and 15:14), expcnt and lgkmcnt left at their maxima
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+}  // namespace dma
+
+template <int MODE>
+__global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int wm = wave / dma::WN, wn = wave % dma::WN;
+    const int b = blockIdx.x;
+    const int per_xcd = a.grid / kXcds;
+    const int lid = (b % kXcds) * per_xcd + b / kXcds;
+    const int n_tiles = a.N / dma::BN;
+    const int slot = lid / n_tiles;
+    if (slot >= a.tiles[0]) return;
+    const int tinfo = a.tiles[1 + slot];
+    const int ei = tinfo >> 16;
+    int mt = tinfo & 0xFFFF, nt = lid % n_tiles;
+    const int entry = a.list.ent[ei];
+    const int e = entry & 1023;
+    const bool shared = e == kSharedTag;
+    const uint8_t* blob = shared ? a.shared_blob : a.slot_base + int64_t(entry >> 10) * a.blob_bytes;
+    const int base = shared ? 0 : a.offsets[e];
+    const int rows = shared ? a.T : a.offsets[e + 1] - base;
+    if (MOE_DMA_NMAJOR) {
+        // within an expert, walk its m-tiles fastest: consecutive workgroups share a weight slice
+        const int mte = (rows + dma::BM - 1) / dma::BM;
+        const int off = lid - n_tiles * (slot - mt);
+        nt = off / mte;
+        mt = off % mte;
+    }
+    const int m0 = mt * dma::BM, n0 = nt * dma::BN;
+    const int K = a.K;
+    const int64_t wrow_bytes = int64_t(K) * 2;
+
+    // per load instruction q of this wave: the lane's global source (k0 = 0) and the wave's LDS offset
+    const uint8_t* src[dma::Q];
+    int ldsoff[dma::Q];
+#pragma unroll
+    for (int q = 0; q < dma::Q; ++q) {
+        const int blk = wave + dma::NW * q;
+        const int J = blk * 64 + lane;                      // 16-byte chunk index within the stage
+        ldsoff[q] = blk * 1024;
+        if (J < dma::BM * 4) {
+            const int r = J / 4, c = (J % 4) ^ ((r >> 2) & 3);
+            int64_t srow;
+            const int rr = m0 + r < rows ? m0 + r : 0;
+            if (MODE == 0)
+                srow = shared ? rr : a.perm[base + rr] / a.k;
+            else
+                srow = shared ? int64_t(a.T) * a.k + rr : base + rr;
+            src[q] = a.a_src + srow * int64_t(K) * 2 + c * 16;
+        } else {
+            const int j = J - dma::BM * 4;
+            const int r = j / 4, c = (j % 4) ^ ((r >> 2) & 3);
+            src[q] = blob + a.off_w + int64_t(n0 + r) * wrow_bytes + c * 16;
+        }
+    }
+    auto issue = [&](int ks) {
+        uint8_t* st = lds8 + (ks % dma::NSTAGE) * dma::STAGE_BYTES;
+#pragma unroll
+        for (int q = 0; q < dma::Q; ++q)
+            __builtin_amdgcn_global_load_lds(src[q] + ks * dma::BK * 2, st + ldsoff[q], 16, 0, 0);
+    };
+
+    typename AccT<dma::MF>::T acc[dma::FM][dma::FN];
+#pragma unroll
+    for (int i = 0; i < dma::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < dma::FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    const int nk = K / dma::BK;
+#pragma unroll
+    for (int s = 0; s < dma::NSTAGE - 1; ++s)
+        if (s < nk) issue(s);
+    for (int ks = 0; ks < nk; ++ks) {
+        // this wave's loads of stage ks have landed; the barrier makes that true for every
+        // wave, and every wave has finished reading stage ks-1 (refilled just below).  A bare
+        // s_barrier: __syncthreads() would also wait for the loads still in flight.
+        if (ks + dma::NSTAGE - 2 < nk) dma::wait_vm<(dma::NSTAGE - 2) * dma::Q>();
+        else dma::wait_vm<0>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (ks + dma::NSTAGE - 1 < nk) issue(ks + dma::NSTAGE - 1);
+        const uint8_t* as_ = lds8 + (ks % dma::NSTAGE) * dma::STAGE_BYTES;
+        const uint8_t* bs_ = as_ + dma::BM * dma::ROWB;
+#pragma unroll
+        for (int kk = 0; kk < dma::BK / 16; ++kk) {
+            bf16x8 af[dma::FM], bfr[dma::FN];
+            const int c = kk * 2 + lane / 32;
+#pragma unroll
+            for (int i = 0; i < dma::FM; ++i) {
+                const int R = wm * dma::TM + i * 32 + lane % 32;
+                af[i] = *reinterpret_cast<const bf16x8*>(as_ + R * dma::ROWB + ((c ^ ((R >> 2) & 3)) << 4));
+            }
+#pragma unroll
+            for (int j = 0; j < dma::FN; ++j) {
+                const int R = wn * dma::TN + j * 32 + lane % 32;
+                bfr[j] = *reinterpret_cast<const bf16x8*>(bs_ + R * dma::ROWB + ((c ^ ((R >> 2) & 3)) << 4));
+            }
+#pragma unroll
+            for (int i = 0; i < dma::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < dma::FN; ++j) acc[i][j] = mfma(af[i], bfr[j], acc[i][j]);
+        }
+    }
+
+    auto row_of = [&](int i, int q) { return m0 + wm * dma::TM + i * 32 + 8 * (q / 4) + (lane / 32) * 4 + (q % 4); };
+    if (MODE == 0) {
+        uint16_t* h = static_cast<uint16_t*>(a.out);
+        const bool gate_lane = (lane % 32) < 16;
+#pragma unroll
+        for (int j = 0; j < dma::FN; ++j) {
+            const int col = (n0 + wn * dma::TN + j * 32) / 32 * 16 + lane % 16;
+#pragma unroll
+            for (int i = 0; i < dma::FM; ++i)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const float up = __shfl_xor(acc[i][j][q], 16, kWave);
+                    const int row = row_of(i, q);
+                    if (gate_lane && row < rows) {
+                        const int64_t hrow = shared ? int64_t(a.T) * a.k + row : base + row;
+                        h[hrow * a.I + col] = dev::f32_to_bf16_bits(ffn::silu(acc[i][j][q]) * up);
+                    }
+                }
+        }
+    } else {
+        float* o = static_cast<float*>(a.out);
+#pragma unroll
+        for (int i = 0; i < dma::FM; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = row_of(i, q);
+                if (row < rows) {
+                    const int64_t p = shared ? int64_t(a.T) * a.k + row : a.perm[base + row];
+#pragma unroll
+                    for (int j = 0; j < dma::FN; ++j) o[p * a.H + n0 + wn * dma::TN + j * 32 + lane % 32] = acc[i][j][q];
+                }
+            }
+    }
+}
+
 // The GEMM stages use more than the default 64 KiB of LDS per workgroup.
 hipError_t allow_lds() {
     static hipError_t once = [] {
@@ -368,6 +560,11 @@ hipError_t allow_lds() {
                              reinterpret_cast<const void*>(&k_gemm<1, false>), reinterpret_cast<const void*>(&k_gemm<1, true>)};
         for (const void* k : ks) {
             hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+            if (e != hipSuccess) return e;
+        }
+        const void* kd[2] = {reinterpret_cast<const void*>(&k_gemm_dma<0>), reinterpret_cast<const void*>(&k_gemm_dma<1>)};
+        for (const void* k : kd) {
+            hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, dma::kLdsBytes);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
@@ -427,12 +624,18 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     a.out = hbuf;
     a.K = c.hidden;
     a.N = 2 * c.inter;
-    a.grid = (mt * (a.N / BN) + kXcds - 1) / kXcds * kXcds;
+    const bool use_dma = MOE_GEMM_DMA && !fp4 && a.N % dma::BN == 0 && a.K % dma::BK == 0;
     if ((e = allow_lds()) != hipSuccess) return e;
-    if (fp4)
-        hipLaunchKernelGGL((k_gemm<0, true>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
-    else
-        hipLaunchKernelGGL((k_gemm<0, false>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
+    if (use_dma) {
+        a.grid = (mt * (a.N / dma::BN) + kXcds - 1) / kXcds * kXcds;
+        hipLaunchKernelGGL((k_gemm_dma<0>), dim3(a.grid), dim3(dma::kThreads), dma::kLdsBytes, s, a);
+    } else {
+        a.grid = (mt * (a.N / BN) + kXcds - 1) / kXcds * kXcds;
+        if (fp4)
+            hipLaunchKernelGGL((k_gemm<0, true>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
+        else
+            hipLaunchKernelGGL((k_gemm<0, false>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // GEMM 2: h [rows x I] . [H x I]^T -> o [pair rows x H]
     a.off_w = lay.d;
@@ -441,11 +644,16 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     a.out = o;
     a.K = c.inter;
     a.N = c.hidden;
-    a.grid = (mt * (a.N / BN) + kXcds - 1) / kXcds * kXcds;
-    if (fp4)
-        hipLaunchKernelGGL((k_gemm<1, true>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
-    else
-        hipLaunchKernelGGL((k_gemm<1, false>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
+    if (MOE_GEMM_DMA && !fp4 && a.N % dma::BN == 0 && a.K % dma::BK == 0) {
+        a.grid = (mt * (a.N / dma::BN) + kXcds - 1) / kXcds * kXcds;
+        hipLaunchKernelGGL((k_gemm_dma<1>), dim3(a.grid), dim3(dma::kThreads), dma::kLdsBytes, s, a);
+    } else {
+        a.grid = (mt * (a.N / BN) + kXcds - 1) / kXcds * kXcds;
+        if (fp4)
+            hipLaunchKernelGGL((k_gemm<1, true>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
+        else
+            hipLaunchKernelGGL((k_gemm<1, false>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
+    }
     return hipGetLastError();
 }
 
