@@ -13,9 +13,11 @@ rotate over the replicas (R emulated layers), so each step's weights come from
 HBM rather than from the 256 MB last-level cache.
 
 Reported besides ``value``:
-  roofline     decode FFN (moe_expert_ffn) bytes / time, timed with HIP events
-               around the FFN of eager steps that each follow a 1 GiB fill (the
-               fill hides the host enqueue time and evicts the last-level cache);
+  roofline     decode FFN (moe_expert_ffn) algorithmic bytes / time per call, timed
+               with HIP events around a graph of FFN calls alone that rotate over
+               the pool replicas; ``traffic`` is the counter-measured HBM bytes per
+               call while the decode kernels are unchanged since the counters;
+  batches      the same step at the other decode batch sizes of the workload;
   cpu_baseline the fp64 oracle timed on the host cores on a bounded sample;
   pipeline     the full cached decode step (GPU route -> host plan with q* ->
                PCIe fills on a side stream + CPU experts -> GPU experts -> merge),
@@ -46,7 +48,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=4000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="a3b_decode_bf16")
-    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--batch", type=int, default=1, help="decode batch of `value`")
+    ap.add_argument("--extra-batches", default="4,8", help="further decode batches reported beside `value` ('' for none)")
     ap.add_argument("--replicas", type=int, default=0, help="slot-pool replicas (0: enough to defeat the 256 MB cache)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -54,6 +57,11 @@ def parse():
     ap.add_argument("--pipeline-steps", type=int, default=400)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-reps", type=int, default=20)
+    ap.add_argument("--stream-layers", type=int, default=4,
+                    help="emulated layers of the streamed prefill chunk (0: skip streaming)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run a plain 256 MiB read + 256 MiB write elementwise kernel (torch.neg), "
+                         "whose byte counters calibrate FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -67,6 +75,31 @@ def payload_bytes(wl):
     return {"f32": 4 * n, "bf16": 2 * n, "mxfp4": n // 2 + n // 32}[wl.wdtype]
 
 
+# HBM traffic of the decode FFN kernels from hardware counters (rocprofv3 --pmc FETCH_SIZE, then
+# --pmc WRITE_SIZE, over `bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-pipeline
+# --prefill-reps 5 --copy-probe`), in KiB per dispatch as the counters read them, summed over
+# k_decode_gate_up and k_decode_down of one moe_expert_ffn call.  The same runs read a plain
+# 256 MiB read + 256 MiB write kernel as FETCH_SIZE 131080 KiB and WRITE_SIZE 262144 KiB, so
+# fetch counts are scaled by 262144 / 131080 and write counts by 1.  A record applies only while
+# the decode kernel sources hash to the value it was taken with.
+DECODE_SOURCES = ("ffn_decode.hip", "ffn_common.h", "device_common.h")
+TRAFFIC = {
+    ("a3b_decode_bf16", 1): {"sha256": "768e8f298aac8d4f21991791b1ad6019b2b622445673198f55c263eb3fb0d613",
+                             "fetch_kib": 24609.1 + 12354.0, "write_kib": 48.0 + 64.0},
+}
+FETCH_FACTOR = 262144.0 / 131080.0
+WRITE_FACTOR = 1.0
+
+
+def decode_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "expert_cached_moe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -77,25 +110,73 @@ def main():
 
     import torch
     import synth
-    from expert_cached_moe_amd import binding as B
-    from expert_cached_moe_amd.runtime import LayerBuffers, pack_pool
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        src = torch.ones(1 << 26, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     wl = synth.workload(args.workload)
     if wl.wdtype == "mxfp4" or not wl.batches:
         raise SystemExit(f"decode bench needs a decode workload, got {wl.name}")
-    Bt, K, W = args.batch, args.steps, args.warmup
+    t0 = time.time()
+    experts = synth.expert_weights_many(wl, range(wl.E + wl.n_shared), threads=16)
+    log(f"expert weights drawn in {time.time() - t0:.1f}s")
+
+    d = decode(args, wl, args.batch, experts)
+    Bt = args.batch
+    result = {"metric": METRIC, "value": d["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": d["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": wl.wdtype, "data": "synthetic",
+              "config": {"workload": f"{wl.name} decode, batch {Bt}", "hidden": wl.H, "inter": wl.I,
+                         "experts": wl.E, "top_k": wl.k, "shared_experts": wl.n_shared, "batch": Bt,
+                         "replicas": d["replicas"], "gpu_experts_per_step": d["gpu_experts_per_step"],
+                         "step": "route+permute+ffn+merge, HIP graph"},
+              "roofline": d["roofline"]}
+    extra = [int(b) for b in args.extra_batches.split(",") if b.strip()] if args.extra_batches else []
+    if extra:
+        result["batches"] = {}
+        for b in extra:
+            e = decode(args, wl, b, experts)
+            result["batches"][str(b)] = {k_: e[k_] for k_ in ("tokens_per_s", "ms_per_step", "gpu_experts_per_step",
+                                                               "replicas")} | {"roofline": e["roofline"]}
+
+    # ---------------------------------------------------------------- 8K prefill chunks (context)
+    if not args.no_prefill:
+        torch.cuda.empty_cache()
+        result["prefill"] = {name: prefill(args, name) for name in ("a3b_prefill8k_bf16", "v4flash_mxfp4")}
+
+    # ---------------------------------------------------------------- full cached pipeline (context)
+    logits, x = d["logits"], d["x"]
+    dt = d["w_dtype"]
+    if not args.no_pipeline:
+        result["pipeline"] = pipeline(args, wl, experts, logits, x, dt)
+
+    # ---------------------------------------------------------------- CPU baseline: the oracle
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, wl, experts, logits, x)
+    print(json.dumps(result), flush=True)
+
+
+def decode(args, wl, Bt, experts):
+    """Decode steps at batch Bt: planner replay, pools, the graph of K timed steps, and the
+    FFN roofline (a graph of FFN calls alone, rotating over the pool replicas)."""
+    import torch
+    import synth
+    from expert_cached_moe_amd import binding as B
+    from expert_cached_moe_amd.runtime import LayerBuffers, pack_pool
+    K, W = args.steps, args.warmup
     dt = {"f32": B.MOE_W_F32, "bf16": B.MOE_W_BF16, "mxfp4": B.MOE_W_MXFP4}[wl.wdtype]
     E, k, H, I = wl.E, wl.k, wl.H, wl.I
     n_trace = wl.steps
 
     # ---------------------------------------------------------------- inputs
-    t0 = time.time()
     logits, _ = synth.zipf_reuse_trace(wl, Bt, n_trace)
     x = synth.activations(wl, n_trace * Bt, tag=11)
-    experts = synth.expert_weights_many(wl, range(E + wl.n_shared), threads=16)
-    log(f"inputs drawn in {time.time() - t0:.1f}s")
 
     # all-resident plan from the library's planner: C = E slots, every miss filled
     cfg_res = B.make_config(H, I, E, k, wl.n_shared, E, 1, dt, 1, 0, 1.0, 1.0)
@@ -111,22 +192,21 @@ def main():
     plans = [B.Plan(cap, E) for _ in range(n_trace)]
     B.moe_lru_replay(planner, 0, ids_all, n_trace, Bt, plans)
     slot_of = B.moe_lru_slots(planner, 0, E)
+    B.moe_destroy(planner)
     step_experts, step_slots = [], []
     for p in plans:
-        ex_ = np.concatenate([p.get("hit"), p.get("fill")]).astype(np.int32)
-        sl_ = np.concatenate([p.get("hit_slot"), p.get("fill_slot")]).astype(np.int32)
-        step_experts.append(ex_)
-        step_slots.append(sl_)
+        step_experts.append(np.concatenate([p.get("hit"), p.get("fill")]).astype(np.int32))
+        step_slots.append(np.concatenate([p.get("hit_slot"), p.get("fill_slot")]).astype(np.int32))
     mean_distinct = float(np.mean([len(e) for e in step_experts]))
 
     # pool laid out by the planner's slots; replicas defeat the last-level cache
-    nb = B.moe_expert_bytes(cfg_res)
     order = [int(np.where(slot_of == s)[0][0]) if (slot_of == s).any() else 0 for s in range(E)]
     host_pool = pack_pool(cfg_res, [experts[e] for e in order], pin=True)
     step_bytes = mean_distinct * payload_bytes(wl) + (payload_bytes(wl) if wl.n_shared else 0)
     R = args.replicas or max(1, math.ceil(4 * MALL_BYTES / step_bytes))
     R = min(R, max(1, int((48 << 30) // host_pool.numel())))
     pools = [host_pool.cuda() for _ in range(R)]
+    del host_pool
     shared = None
     if wl.n_shared:
         sh = pack_pool(cfg_res, [experts[E]], pin=False)
@@ -135,97 +215,79 @@ def main():
     out = torch.empty(Bt * H, dtype=torch.int16 if wl.act_dtype == "bf16" else torch.float32, device="cuda")
     with_shared = 1 if wl.n_shared else 0
     torch.cuda.synchronize()
-    log(f"pool {nb * E / 1e9:.2f} GB x {R} replicas, mean GPU experts/step {mean_distinct:.2f}")
+    log(f"batch {Bt}: pool {B.moe_expert_bytes(cfg_res) * E / 1e9:.2f} GB x {R} replicas, "
+        f"mean GPU experts/step {mean_distinct:.2f}")
 
     # ---------------------------------------------------------------- graph of the timed steps
     stream = torch.cuda.Stream()
     h_ids_steps = [np.ascontiguousarray(ids_all[t]) for t in range(n_trace)]
 
-    def enqueue(s_idx, st, events=None):
-        t = s_idx % n_trace
-        r = s_idx % R
-        L.route(d_logits[t * Bt:(t + 1) * Bt], Bt, st)
-        if events is not None:
-            events[0].record(st)
+    def ffn(s_idx):
+        t, r = s_idx % n_trace, s_idx % R
         L.ffn(d_x[t * Bt:(t + 1) * Bt], Bt, pools[r], step_experts[t], step_slots[t],
-              shared[r] if shared else None, with_shared, st, h_ids=h_ids_steps[t])
-        if events is not None:
-            events[1].record(st)
+              shared[r] if shared else None, with_shared, torch.cuda.current_stream(), h_ids=h_ids_steps[t])
+
+    def enqueue(s_idx):
+        t = s_idx % n_trace
+        st = torch.cuda.current_stream()
+        L.route(d_logits[t * Bt:(t + 1) * Bt], Bt, st)
+        ffn(s_idx)
         L.merge(step_experts[t], with_shared, None, Bt, out, st)
 
-    with torch.cuda.stream(stream):
-        for s in range(min(W, 64)):                     # eager warm-up (code objects, caches)
-            enqueue(s, stream)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for s in range(K):
-            enqueue(W + s, torch.cuda.current_stream())
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):                        # replay runs on the current stream
-        g.replay()                                         # warm-up replay
+    def timed_graph(body, n):
+        """Capture body(W + s) for s < n, replay once to warm up, then time one replay with
+        HIP events recorded on the replay stream; returns milliseconds per iteration."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for s in range(n):
+                body(W + s)
+        t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):                    # replay runs on the current stream
+            g.replay()
+            torch.cuda.synchronize()
+            t_start.record(stream)
+            g.replay()
+            t_end.record(stream)
         torch.cuda.synchronize()
-        t_start.record(stream)
-        g.replay()
-        t_end.record(stream)
+        del g
+        return t_start.elapsed_time(t_end) / n
+
+    with torch.cuda.stream(stream):
+        for s in range(min(W, 64)):                        # eager warm-up (code objects, caches)
+            enqueue(s)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / K
-    value = Bt * K / (total_ms / 1e3)
-    del g
+    ms_per_step = timed_graph(enqueue, K)
+    value = Bt / (ms_per_step / 1e3)
 
     # ---------------------------------------------------------------- decode FFN roofline
-    # Eager steps, each preceded by a 1 GiB fill on the same stream: the fill keeps the
-    # GPU busy while the host enqueues route, event, FFN, event (so the events bracket
-    # the FFN kernels only) and evicts the last-level cache like other layers would.
-    n_prof = min(K, 400)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_prof)]
-    with torch.cuda.stream(stream):
-        for s in range(n_prof):
-            flush.fill_(float(s))
-            enqueue(W + s, stream, ev[s])
-    torch.cuda.synchronize()
-    ffn_ms = sum(a.elapsed_time(b) for a, b in ev) / n_prof
+    # The FFN calls of n_prof consecutive steps alone in one graph: each call reads its
+    # experts from the next pool replica, so the weights come from HBM, and the per-call time
+    # is the two kernels' durations back to back.
+    n_prof = min(K, 1000)
+    ffn_ms = timed_graph(ffn, n_prof)
+    pairs = Bt * k + (Bt if with_shared else 0)
     ffn_bytes = 0.0
     for s in range(n_prof):
-        t = (W + s) % n_trace
-        ne = len(step_experts[t])
-        pairs = Bt * k + (Bt if with_shared else 0)
+        ne = len(step_experts[(W + s) % n_trace])
         ffn_bytes += (ne + with_shared) * payload_bytes(wl) + Bt * H * (2 if wl.act_dtype == "bf16" else 4) + pairs * H * 4
-    achieved = ffn_bytes / n_prof / (ffn_ms / 1e3) / 1e9
-    roofline = {"bound": "hbm", "kernel": "moe_expert_ffn (k_decode_gate_up + k_decode_down)",
+    ffn_bytes /= n_prof
+    achieved = ffn_bytes / (ffn_ms / 1e3) / 1e9
+    rec = TRAFFIC.get((wl.name, Bt))
+    traffic = None
+    if rec is not None and rec["sha256"] == decode_sources_sha256():
+        traffic = round((rec["fetch_kib"] * FETCH_FACTOR + rec["write_kib"] * WRITE_FACTOR) * 1024)
+    roofline = {"bound": "hbm", "kernel": "moe_expert_ffn, decode (k_decode_gate_up + k_decode_down)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "ffn_us": round(ffn_ms * 1e3, 2), "bytes_per_launch": round(ffn_bytes / n_prof),
-                "launches_timed": n_prof}
-    del flush
-    log(f"GPU path: {ms_per_step * 1e3:.2f} us/step, {value:.0f} tok/s; FFN {ffn_ms * 1e3:.2f} us, "
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "ffn_us": round(ffn_ms * 1e3, 3), "bytes_per_launch": round(ffn_bytes), "launches_timed": n_prof}
+    log(f"batch {Bt}: {ms_per_step * 1e3:.2f} us/step, {value:.0f} tok/s; FFN {ffn_ms * 1e3:.2f} us, "
         f"{achieved:.0f} GB/s")
-
-    result = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
-              "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-              "vs_baseline": None, "dtype": wl.wdtype, "data": "synthetic",
-              "config": {"workload": f"{wl.name} decode, batch {Bt}", "hidden": H, "inter": I, "experts": E,
-                         "top_k": k, "shared_experts": wl.n_shared, "batch": Bt, "replicas": R,
-                         "gpu_experts_per_step": round(mean_distinct, 3), "step": "route+permute+ffn+merge, HIP graph"},
-              "roofline": roofline}
-
-    # ---------------------------------------------------------------- 8K prefill chunks (context)
-    if not args.no_prefill:
-        del pools
-        torch.cuda.empty_cache()
-        result["prefill"] = {name: prefill(args, name) for name in ("a3b_prefill8k_bf16", "v4flash_mxfp4")}
-
-    # ---------------------------------------------------------------- full cached pipeline (context)
-    if not args.no_pipeline:
-        result["pipeline"] = pipeline(args, wl, experts, logits, x, dt)
-
-    # ---------------------------------------------------------------- CPU baseline: the oracle
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args, wl, experts, logits, x)
-    B.moe_destroy(planner)
-    print(json.dumps(result), flush=True)
+    L.close()
+    del pools, shared, d_logits, d_x
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": round(value, 1), "ms_per_step": round(ms_per_step, 5), "replicas": R,
+            "gpu_experts_per_step": round(mean_distinct, 3), "roofline": roofline,
+            "logits": logits, "x": x, "w_dtype": dt}
 
 
 def prefill(args, name):
@@ -240,7 +302,8 @@ def prefill(args, name):
     dt = {"f32": B.MOE_W_F32, "bf16": B.MOE_W_BF16, "mxfp4": B.MOE_W_MXFP4}[wl.wdtype]
     cfg = B.make_config(H, I, E, k, wl.n_shared, 0, 1, dt)
     experts = synth.expert_weights_many(wl, range(E + wl.n_shared), threads=16)
-    pool = pack_pool(cfg, [experts[e] for e in range(E)], pin=False).cuda()
+    host_pool = pack_pool(cfg, [experts[e] for e in range(E)], pin=args.stream_layers > 0)
+    pool = host_pool.cuda()
     shared = pack_pool(cfg, [experts[E]], pin=False).cuda() if wl.n_shared else None
     del experts
     L = LayerBuffers(cfg, T)
@@ -290,12 +353,74 @@ def prefill(args, name):
     tflops = flops / (gms / 1e3) / 1e12
     nb = B.moe_expert_bytes(cfg)
     del g
+    res = {"tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_chunk": round(ms, 4), "tokens": T,
+           "gemm_ms": round(gms, 4), "gemm_tflops": round(tflops, 1),
+           "mfma_frac_bf16_peak": round(tflops / 2500.0, 4), "gflop": round(flops / 1e9, 1),
+           "pool_gb": round(nb * E / 1e9, 3), "weights": wl.wdtype,
+           "note": "layer pool resident in HBM; MXFP4 weights dequantised to bf16 MFMA inputs"}
+    del pool
+    if args.stream_layers > 0:
+        res["streamed"] = stream_chunk(args, wl, cfg, host_pool, shared, d_logits, d_x, L, ms)
     L.close()
-    return {"tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_chunk": round(ms, 4), "tokens": T,
-            "gemm_ms": round(gms, 4), "gemm_tflops": round(tflops, 1),
-            "mfma_frac_bf16_peak": round(tflops / 2500.0, 4), "gflop": round(flops / 1e9, 1),
-            "pool_gb": round(nb * E / 1e9, 3), "weights": wl.wdtype,
-            "note": "layer pool resident in HBM; MXFP4 weights dequantised to bf16 MFMA inputs"}
+    return res
+
+
+def stream_chunk(args, wl, cfg, host_pool, shared, d_logits, d_x, L, compute_ms):
+    """The chunk through n emulated layers whose pools upload from pinned host memory
+    (moe_prefill_stream), with two layer buffers and with one (the single-buffer
+    ablation), against the overlap model built from the measured upload and compute."""
+    import torch
+    from expert_cached_moe_amd import binding as B
+    n, T, E = args.stream_layers, wl.T, wl.E
+    nb = B.moe_expert_bytes(cfg)
+    layer_bytes = nb * E
+    scfg = B.make_config(wl.H, wl.I, E, wl.k, wl.n_shared, 0, n, cfg.w_dtype)
+    ctx = B.moe_create(scfg)
+    # every emulated layer streams a full layer pool (the layers hold copies of one pool:
+    # the transfer and the kernels do not depend on the values)
+    hp = torch.empty(n * layer_bytes, dtype=torch.uint8, pin_memory=True)
+    for l in range(n):
+        hp[l * layer_bytes:(l + 1) * layer_bytes].copy_(host_pool)
+    B.moe_bind_pools(ctx, None, 0, hp, n * E)
+    bufs = torch.empty(2 * layer_bytes, dtype=torch.uint8, device="cuda")
+    logits_n = d_logits.repeat(n, 1).contiguous()
+    sh_n = shared.repeat(n).contiguous() if shared is not None else None
+    out = torch.empty(n * T * wl.H, dtype=torch.int16, device="cuda")
+    main, side = torch.cuda.Stream(), torch.cuda.Stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    # B_P: one layer pool, pinned host -> device, on the upload stream
+    ups = []
+    for _ in range(3):
+        e0.record(side)
+        B.moe_upload(ctx, bufs, hp, layer_bytes, side)
+        e1.record(side)
+        torch.cuda.synchronize()
+        ups.append(e0.elapsed_time(e1))
+    up_ms = float(np.median(ups))
+
+    def chunk(n_buf):
+        times = []
+        for _ in range(3):
+            e0.record(main)
+            B.moe_prefill_stream(ctx, bufs, n_buf, logits_n, d_x, T, sh_n, L.ids, L.w, L.counts, L.offsets,
+                                 L.perm, L.inv, L.o, L.ws, out, main, side)
+            e1.record(main)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return float(np.median(times))
+
+    double_ms, single_ms = chunk(2), chunk(1)
+    B.moe_destroy(ctx)
+    pred2 = up_ms + (n - 1) * max(up_ms, compute_ms) + compute_ms
+    pred1 = n * (up_ms + compute_ms)
+    return {"layers": n, "layer_gb": round(layer_bytes / 1e9, 3), "bp_gbps": round(layer_bytes / (up_ms / 1e3) / 1e9, 2),
+            "layer_upload_ms": round(up_ms, 3), "layer_compute_ms": round(compute_ms, 4),
+            "double_ms": round(double_ms, 3), "single_ms": round(single_ms, 3),
+            "double_pred_ms": round(pred2, 3), "single_pred_ms": round(pred1, 3),
+            "chunk_tokens_per_s_double": round(T / (double_ms / 1e3), 1),
+            "single_buffer_penalty": round(1.0 - double_ms / single_ms, 4),
+            "note": "PCIe-inclusive; prediction: double = U + (n-1) max(U, C) + C, single = n (U + C)"}
 
 
 def pipeline(args, wl, experts, logits, x, dt):

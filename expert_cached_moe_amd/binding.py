@@ -34,6 +34,7 @@ EXPORTS = [
     "moe_workspace_bytes", "moe_pair_rows", "moe_pack_expert", "moe_bind_pools", "moe_route",
     "moe_qstar", "moe_lru_step", "moe_lru_replay", "moe_lru_reset", "moe_lru_slots", "moe_lru_stats",
     "moe_fill", "moe_fill_wait", "moe_upload", "moe_expert_ffn", "moe_host_ffn", "moe_merge_partial",
+    "moe_prefill_stream",
 ]
 
 
@@ -77,6 +78,8 @@ _sig = {
     "moe_fill": (ctypes.c_int, [vp, _P(moe_plan), vp]),
     "moe_fill_wait": (ctypes.c_int, [vp, vp]),
     "moe_upload": (ctypes.c_int, [vp, vp, vp, ctypes.c_int64, vp]),
+    "moe_prefill_stream": (ctypes.c_int, [vp, vp, ctypes.c_int32, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, vp, vp]),
     "moe_expert_ffn": (ctypes.c_int, [vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp,
                                       ctypes.c_int32, vp, vp, vp]),
     "moe_host_ffn": (ctypes.c_int, [vp, vp, ctypes.c_int32, vp, vp, _P(moe_plan), vp, ctypes.c_int32]),
@@ -278,6 +281,14 @@ def moe_merge_partial(ctx, d_o, d_topk_ids, d_topk_w, h_gpu_experts, n_gpu, with
     ge = np.ascontiguousarray(h_gpu_experts, dtype=np.int32) if h_gpu_experts is not None else None
     _check(ctx, _lib.moe_merge_partial(ctx, _ptr(d_o), _ptr(d_topk_ids), _ptr(d_topk_w), _ptr(ge), n_gpu,
                                        with_shared, _ptr(d_y_host), T, _ptr(d_out), _stream(s)))
+
+
+def moe_prefill_stream(ctx, d_layer_bufs, n_buffers, d_logits, d_x, T, d_shared, d_topk_ids, d_topk_w, d_counts,
+                       d_offsets, d_perm, d_inv, d_o, d_ws, d_out, s=None, side=None) -> None:
+    _check(ctx, _lib.moe_prefill_stream(ctx, _ptr(d_layer_bufs), n_buffers, _ptr(d_logits), _ptr(d_x), T,
+                                        _ptr(d_shared), _ptr(d_topk_ids), _ptr(d_topk_w), _ptr(d_counts),
+                                        _ptr(d_offsets), _ptr(d_perm), _ptr(d_inv), _ptr(d_o), _ptr(d_ws),
+                                        _ptr(d_out), _stream(s), _stream(side)))
 
 
 def exported_symbols() -> list:

@@ -123,6 +123,8 @@ int moe_create(const moe_config* cfg, moe_ctx** out) {
 void moe_destroy(moe_ctx* ctx) {
     if (!ctx) return;
     if (ctx->fill_event) (void)hipEventDestroy(ctx->fill_event);
+    for (hipEvent_t ev : ctx->stream_ev)
+        if (ev) (void)hipEventDestroy(ev);
     delete ctx;
 }
 

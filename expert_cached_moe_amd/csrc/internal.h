@@ -86,6 +86,8 @@ struct moe_ctx {
     const void* h_pool = nullptr;
     int32_t n_pool = 0;
     hipEvent_t fill_event = nullptr;
+    // layer streaming: [0] start, [1..2] upload into buffer b done, [3..4] compute on buffer b done
+    hipEvent_t stream_ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
     // host FFN workers and scratch
     moe::ThreadPool pool;
     std::vector<float> hx, hh, ho;

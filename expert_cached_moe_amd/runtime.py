@@ -59,12 +59,16 @@ class LayerBuffers:
 
 def pack_pool(cfg: B.moe_config, experts, pin: bool = True) -> torch.Tensor:
     """Pack a sequence of natural-layout expert dicts (wg, wu, wd[, sg, su, sd]) into
-    one contiguous uint8 tensor of blobs (pinned host memory when ``pin``)."""
+    one contiguous uint8 tensor of blobs (pinned host memory when ``pin``).  A ``None``
+    entry leaves its blob filled with 0xFF bytes (NaN in every weight format)."""
     experts = list(experts)
     nb = B.moe_expert_bytes(cfg)
     pool = torch.empty(len(experts) * nb, dtype=torch.uint8, pin_memory=pin)
     view = pool.numpy()
     for i, w in enumerate(experts):
+        if w is None:
+            view[i * nb:(i + 1) * nb] = 0xFF
+            continue
         B.moe_pack_expert(cfg, w["wg"], w["wu"], w["wd"], w.get("sg"), w.get("su"), w.get("sd"),
                           view[i * nb:(i + 1) * nb])
     return pool

@@ -237,6 +237,34 @@ int moe_merge_partial(moe_ctx* ctx, const float* d_o, const int32_t* d_topk_ids,
                       const int32_t* h_gpu_experts, int32_t n_gpu, int32_t with_shared,
                       const float* d_y_host, int32_t T, void* d_out, hipStream_t s);
 
+/* ---------------------------------------------------------------- layer streaming (prefill) */
+/* One T-token prefill chunk through cfg.n_layers MoE layers whose expert pools
+ * stream from the bound host pool (n_layers*E blobs, layer-major, pinned) into
+ * device layer buffers of E blobs each ([A] "Abandoning fixed offloading in favor
+ * of measured bandwidth": full-layer double buffering, the next layer's experts
+ * cross PCIe while the current layer computes).  Layer l runs moe_route on
+ * d_logits + l*T*E, moe_expert_ffn over all E experts of its buffer (slot =
+ * expert) plus, when cfg.n_shared, the shared blob d_shared + l*moe_expert_bytes,
+ * and moe_merge_partial into d_out + l*T*H (activation dtype).
+ *   n_buffers = 2: the upload of layer l+1 runs on `side` while layer l computes
+ *     on `s`; it waits only for the compute of layer l-1 (its buffer's last user).
+ *   n_buffers = 1: the single-buffer ablation; each upload waits for the compute
+ *     of the previous layer.
+ *   d_layer_bufs: n_buffers*E blobs (device, caller-owned);
+ *   d_x [T][H]: the input of every layer (activation dtype);
+ *   d_topk_ids, d_topk_w, d_counts, d_offsets, d_perm, d_inv, d_o, d_ws: as for
+ *     moe_route / moe_expert_ffn with max_T >= T, reused by every layer;
+ *   d_out [n_layers][T][H].
+ * The first upload starts after the work already enqueued on `s`; on return the
+ * whole chunk is enqueued and `s` ends with the last layer's merge.  Requires
+ * moe_bind_pools with a host pool.  Errors found before anything is enqueued:
+ * MOE_EINVAL, MOE_ESTATE (no host pool), MOE_ESHAPE; a HIP error (MOE_EHIP) can
+ * leave part of the chunk enqueued. */
+int moe_prefill_stream(moe_ctx* ctx, void* d_layer_bufs, int32_t n_buffers, const float* d_logits,
+                       const void* d_x, int32_t T, const void* d_shared, int32_t* d_topk_ids, float* d_topk_w,
+                       int32_t* d_counts, int32_t* d_offsets, int32_t* d_perm, int32_t* d_inv, float* d_o,
+                       void* d_ws, void* d_out, hipStream_t s, hipStream_t side);
+
 #ifdef __cplusplus
 }
 #endif

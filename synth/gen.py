@@ -137,8 +137,9 @@ def mxfp4_quantize(w: np.ndarray):
 
 
 # ---------------------------------------------------------------- weights
-def _draw_expert(wl: Workload, e: int):
-    rng = _rng(wl, _WEIGHTS, e)
+def _draw_expert(wl: Workload, e: int, layer: int = 0):
+    # layer 0 keeps the single-layer stream; deeper layers get substreams of their own
+    rng = _rng(wl, _WEIGHTS, e) if layer == 0 else _rng(wl, _WEIGHTS, e, layer)
     H, I = wl.H, wl.I
     wg = rng.standard_normal((I, H), dtype=np.float32) * np.float32(0.02)
     wu = rng.standard_normal((I, H), dtype=np.float32) * np.float32(0.02)
@@ -146,13 +147,14 @@ def _draw_expert(wl: Workload, e: int):
     return wg, wu, wd
 
 
-def expert_weights(wl: Workload, e: int) -> dict:
-    """Natural-layout weights of routed expert ``e`` (``e == E`` is the shared one).
+def expert_weights(wl: Workload, e: int, layer: int = 0) -> dict:
+    """Natural-layout weights of routed expert ``e`` (``e == E`` is the shared one) of MoE
+    layer ``layer``.
 
     Keys: ``wg`` [I,H], ``wu`` [I,H], ``wd`` [H,I] in the storage format
     (float32, or uint16 bf16 bits, or MXFP4 codes) and, for MXFP4, ``sg``,
     ``su``, ``sd`` (e8m0 scales, one per 32 along K)."""
-    wg, wu, wd = _draw_expert(wl, e)
+    wg, wu, wd = _draw_expert(wl, e, layer)
     if wl.wdtype == W_F32:
         return {"wg": wg, "wu": wu, "wd": wd}
     if wl.wdtype == W_BF16:
@@ -163,12 +165,12 @@ def expert_weights(wl: Workload, e: int) -> dict:
     return {"wg": cg, "wu": cu, "wd": cd, "sg": sg, "su": su, "sd": sd}
 
 
-def expert_weights_many(wl: Workload, experts, threads: int = 8) -> dict:
+def expert_weights_many(wl: Workload, experts, threads: int = 8, layer: int = 0) -> dict:
     """expert_weights for several experts, drawn on a thread pool (numpy releases the GIL)."""
     import concurrent.futures as cf
     experts = list(experts)
     with cf.ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
-        return dict(zip(experts, ex.map(lambda e: expert_weights(wl, e), experts)))
+        return dict(zip(experts, ex.map(lambda e: expert_weights(wl, e, layer), experts)))
 
 
 def shared_expert_weights(wl: Workload):

@@ -54,3 +54,19 @@ def rel_err_rows(y, ref):
 def step_ids(logits_step, k):
     ids, gates = oracle.route(logits_step, k)
     return ids, gates
+
+
+def dev_act(x):
+    """Activations to the device: fp32 as is, bf16 bits as int16 storage."""
+    import torch
+    if x.dtype == np.float32:
+        return torch.from_numpy(x).cuda()
+    return torch.from_numpy(x.view(np.int16)).cuda()
+
+
+def out_f64(t, wl, T):
+    """Layer output tensor (fp32, or bf16 bits in int16 storage) as fp64 [T][H]."""
+    a = t.cpu().numpy()
+    if wl.act_dtype == "f32":
+        return a.reshape(T, wl.H).astype(np.float64)
+    return oracle.bf16_bits_to_f64(a.view(np.uint16)).reshape(T, wl.H)

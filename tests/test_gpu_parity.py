@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from helpers import Experts, TOL, config, rel_err_rows
+from helpers import Experts, TOL, config, dev_act, out_f64, rel_err_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -23,18 +23,7 @@ def B():
     return binding
 
 
-def _dev_act(x):
-    """Activations to the device: fp32 as is, bf16 bits as int16 storage."""
-    if x.dtype == np.float32:
-        return torch.from_numpy(x).cuda()
-    return torch.from_numpy(x.view(np.int16)).cuda()
-
-
-def _out_f64(t, wl, T):
-    a = t.cpu().numpy()
-    if wl.act_dtype == "f32":
-        return a.reshape(T, wl.H).astype(np.float64)
-    return oracle.bf16_bits_to_f64(a.view(np.uint16)).reshape(T, wl.H)
+_dev_act, _out_f64 = dev_act, out_f64
 
 
 def _route_case(B, wl, logits, renorm=1):
