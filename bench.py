@@ -77,18 +77,41 @@ def payload_bytes(wl):
 
 # HBM traffic of the decode FFN kernels from hardware counters (rocprofv3 --pmc FETCH_SIZE, then
 # --pmc WRITE_SIZE, over `bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-pipeline
-# --prefill-reps 5 --copy-probe`), in KiB per dispatch as the counters read them, summed over
-# k_decode_gate_up and k_decode_down of one moe_expert_ffn call.  The same runs read a plain
-# 256 MiB read + 256 MiB write kernel as FETCH_SIZE 131080 KiB and WRITE_SIZE 262144 KiB, so
-# fetch counts are scaled by 262144 / 131080 and write counts by 1.  A record applies only while
-# the decode kernel sources hash to the value it was taken with.
+# --prefill-reps 3 --stream-layers 0 --copy-probe`), in KiB per dispatch as the counters read
+# them, summed over k_decode_gate_up and k_decode_down of one moe_expert_ffn call at batch 1
+# (every call has 8 experts).  The same runs read the plain 256 MiB read + 256 MiB write kernel
+# of --copy-probe as FETCH_SIZE 131080 KiB and WRITE_SIZE 262144 KiB, so fetch counts are scaled
+# by 262144 / 131080 and write counts by 1.  A record applies only while the decode kernel
+# sources hash to the value it was taken with.
 DECODE_SOURCES = ("ffn_decode.hip", "ffn_common.h", "device_common.h")
 TRAFFIC = {
     ("a3b_decode_bf16", 1): {"sha256": "768e8f298aac8d4f21991791b1ad6019b2b622445673198f55c263eb3fb0d613",
-                             "fetch_kib": 24609.1 + 12354.0, "write_kib": 48.0 + 64.0},
+                             "fetch_kib": 24608.8 + 12354.0, "write_kib": 48.0 + 64.0},
 }
 FETCH_FACTOR = 262144.0 / 131080.0
 WRITE_FACTOR = 1.0
+
+
+class _phase:
+    """A named range around a bench phase (roctx through torch's marker API when the build
+    has it), so that a kernel trace taken with rocprofv3 --marker-trace can be split by phase."""
+
+    def __init__(self, name):
+        self.name = name
+
+    def __enter__(self):
+        try:
+            import torch
+            torch.cuda.nvtx.range_push(self.name)
+            self.on = True
+        except Exception:
+            self.on = False
+
+    def __exit__(self, *exc):
+        if self.on:
+            import torch
+            torch.cuda.synchronize()
+            torch.cuda.nvtx.range_pop()
 
 
 def decode_sources_sha256():
@@ -127,7 +150,8 @@ def main():
     experts = synth.expert_weights_many(wl, range(wl.E + wl.n_shared), threads=16)
     log(f"expert weights drawn in {time.time() - t0:.1f}s")
 
-    d = decode(args, wl, args.batch, experts)
+    with _phase(f"decode batch {args.batch}"):
+        d = decode(args, wl, args.batch, experts)
     Bt = args.batch
     result = {"metric": METRIC, "value": d["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
               "warmup": args.warmup, "ms_per_step": d["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -141,20 +165,25 @@ def main():
     if extra:
         result["batches"] = {}
         for b in extra:
-            e = decode(args, wl, b, experts)
+            with _phase(f"decode batch {b}"):
+                e = decode(args, wl, b, experts)
             result["batches"][str(b)] = {k_: e[k_] for k_ in ("tokens_per_s", "ms_per_step", "gpu_experts_per_step",
                                                                "replicas")} | {"roofline": e["roofline"]}
 
     # ---------------------------------------------------------------- 8K prefill chunks (context)
     if not args.no_prefill:
         torch.cuda.empty_cache()
-        result["prefill"] = {name: prefill(args, name) for name in ("a3b_prefill8k_bf16", "v4flash_mxfp4")}
+        result["prefill"] = {}
+        for name in ("a3b_prefill8k_bf16", "v4flash_mxfp4"):
+            with _phase(f"prefill {name}"):
+                result["prefill"][name] = prefill(args, name)
 
     # ---------------------------------------------------------------- full cached pipeline (context)
     logits, x = d["logits"], d["x"]
     dt = d["w_dtype"]
     if not args.no_pipeline:
-        result["pipeline"] = pipeline(args, wl, experts, logits, x, dt)
+        with _phase("cached decode pipeline"):
+            result["pipeline"] = pipeline(args, wl, experts, logits, x, dt)
 
     # ---------------------------------------------------------------- CPU baseline: the oracle
     if not args.no_cpu_baseline:
