@@ -76,12 +76,12 @@ template <> struct AccT<32> { typedef f32x16 T; };
 
 struct TileMapArgs {
     const int32_t* offsets;
-    int32_t T, n_shared_tiles;
+    int32_t T, bm;            // bm: row-tile height of the GEMM kernel that reads the list
     int32_t* tiles;   // [0]: count, then (entry << 16) | m_tile
     ExpertList list;
 };
 
-// Tiles of every listed expert in list order: ceil(rows / BM) m-tiles each.
+// Tiles of every listed expert in list order: ceil(rows / bm) m-tiles each.
 __global__ void __launch_bounds__(1024) k_tile_map(const TileMapArgs a) {
     __shared__ int32_t s_cnt[kMaxExperts + 1];
     __shared__ int32_t s_base[kMaxExperts + 2];
@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(1024) k_tile_map(const TileMapArgs a) {
     for (int i = tid; i < n; i += blockDim.x) {
         const int e = a.list.ent[i] & 1023;
         const int rows = e == kSharedTag ? a.T : a.offsets[e + 1] - a.offsets[e];
-        s_cnt[i] = (rows + BM - 1) / BM;
+        s_cnt[i] = (rows + a.bm - 1) / a.bm;
     }
     __syncthreads();
     if (tid < kWave) {                        // exclusive scan, 9 entries per lane
@@ -390,20 +390,58 @@ __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
 #ifndef MOE_DMA_STAGES
 #define MOE_DMA_STAGES 3
 #endif
+#ifndef MOE_DMA_BK
+#define MOE_DMA_BK 32
+#endif
+#ifndef MOE_DMA_WSKIP
+#define MOE_DMA_WSKIP 1
+#endif
+#ifndef MOE_DMA_WM
+#define MOE_DMA_WM 2
+#endif
+#ifndef MOE_DMA_WN
+#define MOE_DMA_WN 4
+#endif
 #ifndef MOE_DMA_NMAJOR
 #define MOE_DMA_NMAJOR 0
 #endif
 namespace dma {
-constexpr int BM = MOE_DMA_BM, BN = MOE_DMA_BN, WM = 2, WN = 4, MF = 32, BK = 32, NSTAGE = MOE_DMA_STAGES;
+constexpr int BM = MOE_DMA_BM, BN = MOE_DMA_BN, WM = MOE_DMA_WM, WN = MOE_DMA_WN, MF = 32, BK = MOE_DMA_BK,
+              NSTAGE = MOE_DMA_STAGES;
 constexpr int kThreads = WM * WN * 64, NW = WM * WN;
 constexpr int TM = BM / WM, TN = BN / WN, FM = TM / MF, FN = TN / MF;
 constexpr int ROWB = BK * 2;                              // bytes per LDS row
+constexpr int CPR = ROWB / 16;                            // 16-byte chunks per row
+static_assert(CPR == 4 || CPR == 8, "K slice of 32 or 64");
 constexpr int STAGE_BYTES = (BM + BN) * ROWB;
 constexpr int Q = (BM + BN) * ROWB / 1024 / NW;           // 1 KiB load instructions per wave per stage
-constexpr int kLdsBytes = NSTAGE * STAGE_BYTES;
+constexpr int kStageLds = NSTAGE * STAGE_BYTES;
+// Epilogue staging.  GEMM 1: the tile's h values, BM rows of BN/2 bf16; the row stride is
+// 16 bytes past a multiple of 64 so the four rows one store instruction touches fall in
+// different bank groups.  GEMM 2: fp32 rows in passes of PR rows (stride 32 bytes past a
+// multiple of 64: the two rows of one store land in opposite bank halves) and the rows'
+// destinations.  The staging may not push the workgroup past the LDS that keeps its
+// occupancy (80 KiB when the stages allow two workgroups per CU, else 160 KiB).
+constexpr int HSTR = BN + 16;
+constexpr int OSTR = BN * 4 + 32;
+constexpr int kLdsCap = kStageLds <= 80 * 1024 ? 80 * 1024 : 160 * 1024;
+constexpr int pass_rows() {
+    int pr = BM;
+    while (pr > 32 && pr * OSTR + BM * 4 > (kStageLds > kLdsCap ? kStageLds : kLdsCap)) pr /= 2;
+    return pr;
+}
+constexpr int PR = pass_rows();
+constexpr int kEpiLds = BM * HSTR > PR * OSTR + BM * 4 ? BM * HSTR : PR * OSTR + BM * 4;
+constexpr int kLdsBytes = kStageLds > kEpiLds ? kStageLds : kEpiLds;
+static_assert(PR % 32 == 0 && BM % PR == 0, "epilogue passes hold whole fragments");
 static_assert(Q * NW * 1024 == STAGE_BYTES, "stage split");
-static_assert(BM == ::moe::BM, "the tile list is built with the same row-tile height for every GEMM kernel");
+static_assert(FM * MF == TM && FN * MF == TN, "wave tile");
+static_assert((NSTAGE - 1) * Q < 64, "vmcnt range");
 static_assert((BM * ROWB) % 1024 == 0, "A/B boundary on a load block");
+
+// LDS position of 16-byte chunk c of row r: 64 B rows put 4 rows side by side in the 256 B
+// bank window, 128 B rows 2, so the XOR spreads the 32 rows of a fragment read over all banks.
+__device__ __forceinline__ int swz(int r, int c) { return CPR == 4 ? c ^ ((r >> 2) & 3) : c ^ ((r >> 1) & 7); }
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -451,8 +489,8 @@ __global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
         const int blk = wave + dma::NW * q;
         const int J = blk * 64 + lane;                      // 16-byte chunk index within the stage
         ldsoff[q] = blk * 1024;
-        if (J < dma::BM * 4) {
-            const int r = J / 4, c = (J % 4) ^ ((r >> 2) & 3);
+        if (J < dma::BM * dma::CPR) {
+            const int r = J / dma::CPR, c = dma::swz(r, J % dma::CPR);
             int64_t srow;
             const int rr = m0 + r < rows ? m0 + r : 0;
             if (MODE == 0)
@@ -461,8 +499,8 @@ __global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
                 srow = shared ? int64_t(a.T) * a.k + rr : base + rr;
             src[q] = a.a_src + srow * int64_t(K) * 2 + c * 16;
         } else {
-            const int j = J - dma::BM * 4;
-            const int r = j / 4, c = (j % 4) ^ ((r >> 2) & 3);
+            const int j = J - dma::BM * dma::CPR;
+            const int r = j / dma::CPR, c = dma::swz(r, j % dma::CPR);
             src[q] = blob + a.off_w + int64_t(n0 + r) * wrow_bytes + c * 16;
         }
     }
@@ -482,6 +520,8 @@ __global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
     const int nk = K / dma::BK;
+    // a wave whose rows all lie past the expert's last row only helps load and keeps the barriers
+    const bool active = !MOE_DMA_WSKIP || m0 + wm * dma::TM < rows;
 #pragma unroll
     for (int s = 0; s < dma::NSTAGE - 1; ++s)
         if (s < nk) issue(s);
@@ -497,6 +537,7 @@ __global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
         if (ks + dma::NSTAGE - 1 < nk) issue(ks + dma::NSTAGE - 1);
         const uint8_t* as_ = lds8 + (ks % dma::NSTAGE) * dma::STAGE_BYTES;
         const uint8_t* bs_ = as_ + dma::BM * dma::ROWB;
+        if (!active) continue;
 #pragma unroll
         for (int kk = 0; kk < dma::BK / 16; ++kk) {
             bf16x8 af[dma::FM], bfr[dma::FN];
@@ -504,12 +545,12 @@ __global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
 #pragma unroll
             for (int i = 0; i < dma::FM; ++i) {
                 const int R = wm * dma::TM + i * 32 + lane % 32;
-                af[i] = *reinterpret_cast<const bf16x8*>(as_ + R * dma::ROWB + ((c ^ ((R >> 2) & 3)) << 4));
+                af[i] = *reinterpret_cast<const bf16x8*>(as_ + R * dma::ROWB + (dma::swz(R, c) << 4));
             }
 #pragma unroll
             for (int j = 0; j < dma::FN; ++j) {
                 const int R = wn * dma::TN + j * 32 + lane % 32;
-                bfr[j] = *reinterpret_cast<const bf16x8*>(bs_ + R * dma::ROWB + ((c ^ ((R >> 2) & 3)) << 4));
+                bfr[j] = *reinterpret_cast<const bf16x8*>(bs_ + R * dma::ROWB + (dma::swz(R, c) << 4));
             }
 #pragma unroll
             for (int i = 0; i < dma::FM; ++i)
@@ -518,38 +559,78 @@ __global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
         }
     }
 
-    auto row_of = [&](int i, int q) { return m0 + wm * dma::TM + i * 32 + 8 * (q / 4) + (lane / 32) * 4 + (q % 4); };
+    // Epilogue through LDS: once every wave is past the last K step (no loads in flight) the
+    // stages are free; the tile is staged there and written out as whole rows, 16 bytes a lane.
+    const int tid_ = threadIdx.x;
+    __syncthreads();
     if (MODE == 0) {
-        uint16_t* h = static_cast<uint16_t*>(a.out);
-        const bool gate_lane = (lane % 32) < 16;
-#pragma unroll
-        for (int j = 0; j < dma::FN; ++j) {
-            const int col = (n0 + wn * dma::TN + j * 32) / 32 * 16 + lane % 16;
+        // SwiGLU: in a 32-wide fragment lanes 0-15 hold gate and lanes 16-31 up for the same 16
+        // h columns.  permlane16_swap of elements q1 and q1+4 hands every lane a (gate, up)
+        // pair: lanes 0-15 of each half those of q1, lanes 16-31 those of q1+4.
+        uint8_t* ht = lds8;
+        if (active) {
 #pragma unroll
             for (int i = 0; i < dma::FM; ++i)
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const float up = __shfl_xor(acc[i][j][q], 16, kWave);
-                    const int row = row_of(i, q);
-                    if (gate_lane && row < rows) {
-                        const int64_t hrow = shared ? int64_t(a.T) * a.k + row : base + row;
-                        h[hrow * a.I + col] = dev::f32_to_bf16_bits(ffn::silu(acc[i][j][q]) * up);
+                for (int j = 0; j < dma::FN; ++j) {
+                    const int col = (wn * dma::TN + j * 32) / 2 + lane % 16;
+#pragma unroll
+                    for (int qq = 0; qq < 8; ++qq) {
+                        const int q1 = (qq / 4) * 8 + qq % 4;
+                        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i][j][q1]),
+                                                                         __float_as_uint(acc[i][j][q1 + 4]), false, false);
+                        const float g = __uint_as_float(sw[0]), u = __uint_as_float(sw[1]);
+                        const int q = (lane % 32) < 16 ? q1 : q1 + 4;
+                        const int r = wm * dma::TM + i * 32 + 8 * (q / 4) + (lane / 32) * 4 + (q % 4);
+                        *reinterpret_cast<uint16_t*>(ht + r * dma::HSTR + col * 2) =
+                            dev::f32_to_bf16_bits(ffn::silu(g) * u);
                     }
                 }
         }
+        __syncthreads();
+        constexpr int CH = dma::BN / 16;                     // 16-byte chunks per h row of the tile
+        uint16_t* h = static_cast<uint16_t*>(a.out);
+        for (int idx = tid_; idx < dma::BM * CH; idx += dma::kThreads) {
+            const int r = idx / CH, c = idx % CH;
+            if (m0 + r < rows) {
+                const int64_t hrow = shared ? int64_t(a.T) * a.k + m0 + r : base + m0 + r;
+                *reinterpret_cast<dev::u32x4*>(h + hrow * a.I + n0 / 2 + c * 8) =
+                    *reinterpret_cast<const dev::u32x4*>(ht + r * dma::HSTR + c * 16);
+            }
+        }
     } else {
+        uint8_t* ot = lds8;
+        int32_t* dst = reinterpret_cast<int32_t*>(lds8 + dma::PR * dma::OSTR);
+        for (int r = tid_; r < dma::BM; r += dma::kThreads)
+            dst[r] = m0 + r >= rows ? -1 : shared ? a.T * a.k + m0 + r : a.perm[base + m0 + r];
         float* o = static_cast<float*>(a.out);
+        constexpr int CH = dma::BN / 4;                      // 16-byte chunks per fp32 row of the tile
+        for (int pass = 0; pass < dma::BM / dma::PR; ++pass) {
+            if (active) {
 #pragma unroll
-        for (int i = 0; i < dma::FM; ++i)
+                for (int i = 0; i < dma::FM; ++i) {
+                    const int r0 = wm * dma::TM + i * 32;
+                    if (r0 / dma::PR != pass) continue;
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int row = row_of(i, q);
-                if (row < rows) {
-                    const int64_t p = shared ? int64_t(a.T) * a.k + row : a.perm[base + row];
+                    for (int j = 0; j < dma::FN; ++j)
 #pragma unroll
-                    for (int j = 0; j < dma::FN; ++j) o[p * a.H + n0 + wn * dma::TN + j * 32 + lane % 32] = acc[i][j][q];
+                        for (int q = 0; q < 16; ++q) {
+                            const int r = r0 - pass * dma::PR + 8 * (q / 4) + (lane / 32) * 4 + (q % 4);
+                            *reinterpret_cast<float*>(ot + r * dma::OSTR + (wn * dma::TN + j * 32 + lane % 32) * 4) =
+                                acc[i][j][q];
+                        }
                 }
             }
+            __syncthreads();
+            for (int idx = tid_; idx < dma::PR * CH; idx += dma::kThreads) {
+                const int r = idx / CH, c = idx % CH;
+                const int d = dst[pass * dma::PR + r];
+                if (d >= 0)
+                    *reinterpret_cast<dev::u32x4*>(o + int64_t(d) * a.H + n0 + c * 4) =
+                        *reinterpret_cast<const dev::u32x4*>(ot + r * dma::OSTR + c * 16);
+            }
+            __syncthreads();
+        }
     }
 }
 
@@ -572,14 +653,16 @@ hipError_t allow_lds() {
     return once;
 }
 
-int max_tiles(const moe_config& c, int32_t T) {
+// Upper bound on the tile count of a list built with row-tile height bm (every expert may
+// add one partial tile, and the shared expert's T rows one more).
+int max_tiles(const moe_config& c, int32_t T, int bm) {
     const int64_t pairs = int64_t(T) * c.top_k;
-    return int((pairs + BM - 1) / BM + c.n_experts + 1 + (T + BM - 1) / BM + 1);
+    return int((pairs + bm - 1) / bm + c.n_experts + 1 + (T + bm - 1) / bm + 1);
 }
 
 }  // namespace
 
-int64_t gemm_tile_ints(const moe_config& c, int32_t T) { return 1 + max_tiles(c, T); }
+int64_t gemm_tile_ints(const moe_config& c, int32_t T) { return 1 + max_tiles(c, T, BM < dma::BM ? BM : dma::BM); }
 
 bool gemm_shape_supported(const moe_config& c) {
     if (c.w_dtype == MOE_W_F32) return false;
@@ -592,18 +675,19 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
                            const void* shared, const ExpertList& list, float* o, void* ws, hipStream_t s) {
     const WsLayout W = ws_layout(c, T);
     int32_t* tiles = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + W.tiles);
+    const bool fp4 = c.w_dtype == MOE_W_MXFP4;
+    const bool dma1 = MOE_GEMM_DMA && !fp4 && (2 * c.inter) % dma::BN == 0 && c.hidden % dma::BK == 0;
+    const bool dma2 = MOE_GEMM_DMA && !fp4 && c.hidden % dma::BN == 0 && c.inter % dma::BK == 0;
     TileMapArgs tm;
     tm.offsets = offsets;
     tm.T = T;
-    tm.n_shared_tiles = 0;
+    tm.bm = dma1 ? dma::BM : BM;
     tm.tiles = tiles;
     tm.list = list;
     hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, s, tm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-
-    const int mt = max_tiles(c, T);
-    const bool fp4 = c.w_dtype == MOE_W_MXFP4;
+    const int mt1 = max_tiles(c, T, tm.bm);
     GemmArgs a;
     a.slot_base = static_cast<const uint8_t*>(slot_base);
     a.shared_blob = static_cast<const uint8_t*>(shared);
@@ -624,13 +708,12 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     a.out = hbuf;
     a.K = c.hidden;
     a.N = 2 * c.inter;
-    const bool use_dma = MOE_GEMM_DMA && !fp4 && a.N % dma::BN == 0 && a.K % dma::BK == 0;
     if ((e = allow_lds()) != hipSuccess) return e;
-    if (use_dma) {
-        a.grid = (mt * (a.N / dma::BN) + kXcds - 1) / kXcds * kXcds;
+    if (dma1) {
+        a.grid = (mt1 * (a.N / dma::BN) + kXcds - 1) / kXcds * kXcds;
         hipLaunchKernelGGL((k_gemm_dma<0>), dim3(a.grid), dim3(dma::kThreads), dma::kLdsBytes, s, a);
     } else {
-        a.grid = (mt * (a.N / BN) + kXcds - 1) / kXcds * kXcds;
+        a.grid = (mt1 * (a.N / BN) + kXcds - 1) / kXcds * kXcds;
         if (fp4)
             hipLaunchKernelGGL((k_gemm<0, true>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
         else
@@ -644,11 +727,18 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     a.out = o;
     a.K = c.inter;
     a.N = c.hidden;
-    if (MOE_GEMM_DMA && !fp4 && a.N % dma::BN == 0 && a.K % dma::BK == 0) {
-        a.grid = (mt * (a.N / dma::BN) + kXcds - 1) / kXcds * kXcds;
+    const int bm2 = dma2 ? dma::BM : BM;
+    if (bm2 != tm.bm) {            // the list is rebuilt after GEMM 1 has read it (same stream)
+        tm.bm = bm2;
+        hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, s, tm);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const int mt2 = max_tiles(c, T, bm2);
+    if (dma2) {
+        a.grid = (mt2 * (a.N / dma::BN) + kXcds - 1) / kXcds * kXcds;
         hipLaunchKernelGGL((k_gemm_dma<1>), dim3(a.grid), dim3(dma::kThreads), dma::kLdsBytes, s, a);
     } else {
-        a.grid = (mt * (a.N / BN) + kXcds - 1) / kXcds * kXcds;
+        a.grid = (mt2 * (a.N / BN) + kXcds - 1) / kXcds * kXcds;
         if (fp4)
             hipLaunchKernelGGL((k_gemm<1, true>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
         else
