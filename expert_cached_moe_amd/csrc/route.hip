@@ -8,12 +8,14 @@
 //
 // Selection order: logit descending, lower expert id on equal logits (-0 == +0).
 // Gates: softmax renormalised over the k selected logits (or over all experts).
+// Selection: k rounds of a wave-wide maximum over 64-bit keys that pack an
+// order-preserving key of the logit with the inverted expert id, so the order is
+// one integer compare and every lane ends each round holding the winner.
 // Grouping: stable counting sort of pairs p = t*k + j by expert (ascending p
 // within an expert), with its inverse.  Integer work is exact and deterministic:
 // counts use integer LDS atomics, ranks use wave ballots.
 #include <hip/hip_runtime.h>
 
-#include <climits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -27,70 +29,83 @@ constexpr int kRouteWaves = 16;              // tokens per workgroup in the larg
 constexpr int kBlock = kRouteWaves * kWave;  // 1024 threads
 static_assert(kBlock == kPermChunk, "one pair per thread per permutation chunk");
 
-// (value, id) arg-max step: take the other candidate if it ranks first
-// (larger logit, or equal logit and lower id).  Empty candidates are (-inf, INT_MAX).
-__device__ __forceinline__ void take_better(float& v, int& e, float ov, int oe) {
-    if (ov > v || (ov == v && oe < e)) {
-        v = ov;
-        e = oe;
-    }
+// Order-preserving key of a logit: larger logit -> larger unsigned key; -0 and +0 share a key.
+__device__ __forceinline__ uint32_t order_key(float v) {
+    const uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// (logit key, inverted id) as one 64-bit key, split in halves: a larger key ranks first
+// (larger logit, then lower id).  0 marks an expert that is out of the running.
+struct Key64 {
+    uint32_t hi, lo;
+};
+__device__ __forceinline__ bool key_gt(Key64 a, Key64 b) { return a.hi > b.hi || (a.hi == b.hi && a.lo > b.lo); }
+__device__ __forceinline__ void key_max(Key64& a, Key64 b) {
+    const bool g = key_gt(b, a);
+    a.hi = g ? b.hi : a.hi;
+    a.lo = g ? b.lo : a.lo;
+}
 template <int CTRL>
-__device__ __forceinline__ void dpp_step(float& v, int& e) {
-    const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-    const int oe = __builtin_amdgcn_mov_dpp(e, CTRL, 0xF, 0xF, false);
-    take_better(v, e, ov, oe);
+__device__ __forceinline__ void key_dpp_max(Key64& a) {
+    Key64 b;
+    b.hi = uint32_t(__builtin_amdgcn_mov_dpp(int(a.hi), CTRL, 0xF, 0xF, false));
+    b.lo = uint32_t(__builtin_amdgcn_mov_dpp(int(a.lo), CTRL, 0xF, 0xF, false));
+    key_max(a, b);
 }
 
-// Wave-wide arg-max: butterflies inside each row of 16 lanes with DPP (quad swaps,
-// then rotations by 4 and 8), then the four row winners through readlane.  The
-// result is uniform across the wave.
-__device__ __forceinline__ void wave_argmax(float& v, int& e) {
-    dpp_step<0xB1>(v, e);   // quad_perm [1,0,3,2]
-    dpp_step<0x4E>(v, e);   // quad_perm [2,3,0,1]
-    dpp_step<0x124>(v, e);  // row_ror:4
-    dpp_step<0x128>(v, e);  // row_ror:8
-    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    int be = __builtin_amdgcn_readlane(e, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r)
-        take_better(bv, be, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r)),
-                    __builtin_amdgcn_readlane(e, 16 * r));
-    v = bv;
-    e = be;
+// Wave-wide maximum of a key, left in every lane: butterflies inside each row of 16 lanes
+// (DPP quad swaps, rotations by 4 and 8), then row pairs and wave halves exchanged with
+// permlane16_swap / permlane32_swap.
+__device__ __forceinline__ Key64 wave_max(Key64 a) {
+    key_dpp_max<0xB1>(a);   // quad_perm [1,0,3,2]
+    key_dpp_max<0x4E>(a);   // quad_perm [2,3,0,1]
+    key_dpp_max<0x124>(a);  // row_ror:4
+    key_dpp_max<0x128>(a);  // row_ror:8
+    const auto h16 = __builtin_amdgcn_permlane16_swap(a.hi, a.hi, false, false);
+    const auto l16 = __builtin_amdgcn_permlane16_swap(a.lo, a.lo, false, false);
+    a = Key64{h16[0], l16[0]};
+    key_max(a, Key64{h16[1], l16[1]});
+    const auto h32 = __builtin_amdgcn_permlane32_swap(a.hi, a.hi, false, false);
+    const auto l32 = __builtin_amdgcn_permlane32_swap(a.lo, a.lo, false, false);
+    a = Key64{h32[0], l32[0]};
+    key_max(a, Key64{h32[1], l32[1]});
+    return a;
 }
 
-// Route one token with one wave.  EPL = experts per lane (ceil(E/64)).
+// Route one token with one wave.  EPL = experts per lane (ceil(E/64)); lane l holds experts
+// l + 64 i.  k rounds of a wave-wide maximum over the packed keys; lane j keeps the j-th pick.
 template <int EPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ lrow, int E, int k, int renorm,
                                             int32_t* __restrict__ ids_out, float* __restrict__ w_out,
                                             int32_t* __restrict__ lds_ids) {
     const int lane = dev::lane_id();
     float v[EPL];
-    bool live[EPL];
+    Key64 key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + kWave * i;
-        live[i] = e < E;
-        v[i] = live[i] ? lrow[e] : 0.0f;
+        const bool live = e < E;
+        v[i] = live ? lrow[e] : 0.0f;
+        key[i] = live ? Key64{order_key(v[i]), ~uint32_t(e)} : Key64{0u, 0u};
     }
-    // k rounds of a wave-wide arg-max; lane j keeps the j-th selection.
-    float my_v = 0.0f, v0 = 0.0f;
-    int my_e = -1;
+    Key64 mine{0u, 0u};
     for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int be = INT_MAX;
+        Key64 best = key[0];
+#pragma unroll
+        for (int i = 1; i < EPL; ++i) key_max(best, key[i]);
+        best = wave_max(best);
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
-            if (live[i]) take_better(bv, be, v[i], lane + kWave * i);
-        wave_argmax(bv, be);
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (lane + kWave * i == be) live[i] = false;
-        if (j == 0) v0 = bv;
-        if (lane == j) { my_v = bv; my_e = be; }
+            if (key[i].hi == best.hi && key[i].lo == best.lo) key[i] = Key64{0u, 0u};
+        if (lane == j) mine = best;
     }
+    const float my_v = key_value(mine.hi);
+    const int my_e = int(~mine.lo);
+    const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
     // softmax over the selected logits (or over all E), shifted by the largest logit
     const float ex = lane < k ? expf(my_v - v0) : 0.0f;
     float den = 0.0f;
@@ -241,16 +256,16 @@ __global__ __launch_bounds__(kBlock) void k_route_small(const float* __restrict_
 // pair of lane p with expert e: eq = lanes with expert e, lt = lanes with a smaller
 // expert (bit-serial compare of the 10-bit ids, most significant bit first), so
 // its position is |lt| + |eq below p|.
-__global__ __launch_bounds__(256) void k_route_tiny(const float* __restrict__ logits, int T, int E, int k,
-                                                    int renorm, int32_t* __restrict__ ids, float* __restrict__ w,
-                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+__global__ __launch_bounds__(1024) void k_route_tiny(const float* __restrict__ logits, int T, int E, int k,
+                                                     int renorm, int32_t* __restrict__ ids, float* __restrict__ w,
+                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
     __shared__ int32_t s_ids[kWave];
     const int tid = threadIdx.x;
-    route_dispatch(logits, T, E, k, renorm, 0, 4, ids, w, s_ids);
+    route_dispatch(logits, T, E, k, renorm, 0, blockDim.x / kWave, ids, w, s_ids);
     __syncthreads();
     const int n = T * k;
-    for (int e = tid; e < E; e += 256) {
+    for (int e = tid; e < E; e += blockDim.x) {
         int c = 0, lt = 0;
         for (int p = 0; p < n; ++p) {
             const int v = s_ids[p];
@@ -364,8 +379,9 @@ hipError_t launch_route(const moe_config& c, const float* logits, int32_t T, int
     const int E = c.n_experts, k = c.top_k;
     const int64_t n = int64_t(T) * k;
     if (n <= kWave) {
-        hipLaunchKernelGGL(k_route_tiny, dim3(1), dim3(256), 0, s, logits, T, E, k, c.renormalize, ids, w, counts,
-                           offsets, perm, inv);
+        const int waves = T < 1 ? 1 : T > 16 ? 16 : int(T);   // one wave per token
+        hipLaunchKernelGGL(k_route_tiny, dim3(1), dim3(waves * kWave), 0, s, logits, T, E, k, c.renormalize, ids, w,
+                           counts, offsets, perm, inv);
         return hipGetLastError();
     }
     if (n <= kSmallRouteMaxPairs) {
