@@ -37,6 +37,11 @@ __global__ void __launch_bounds__(256) k_merge(const MergeArgs a) {
                        : make_float4(0.f, 0.f, 0.f, 0.f);
     float g[kMaxTopK];
     int64_t row[kMaxTopK];
+    // the mask words are read up front and picked by compare, so the only memory access
+    // that waits for an id is none
+    uint32_t mw[kMaxExperts / 32];
+#pragma unroll
+    for (int q = 0; q < kMaxExperts / 32; ++q) mw[q] = a.mask[q];
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
         row[j] = -1;
@@ -44,7 +49,10 @@ __global__ void __launch_bounds__(256) k_merge(const MergeArgs a) {
         if (j < a.k) {
             const int p = t * a.k + j;
             const int e = a.ids[p];
-            if ((a.mask[e >> 5] >> (e & 31)) & 1u) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int q = 0; q < kMaxExperts / 32; ++q) word = (e >> 5) == q ? mw[q] : word;
+            if ((word >> (e & 31)) & 1u) {
                 row[j] = p;
                 g[j] = a.w[p];
             }
