@@ -378,12 +378,25 @@ def prefill(args, name):
             torch.cuda.synchronize()
             gemm_ms.append(ev[0].elapsed_time(ev[1]))
     gms = float(np.median(gemm_ms))
+    # router logits of the chunk (moe_router_logits), context: the chunk itself starts from logits
+    d_wr = torch.from_numpy(np.ascontiguousarray(synth.router_weights(wl).T)).cuda()
+    lg = torch.empty(T * E, dtype=torch.float32, device="cuda")
+    rl_ms = []
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            ev[0].record(stream)
+            B.moe_router_logits(L.ctx, d_x, T, d_wr, lg, stream)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            rl_ms.append(ev[0].elapsed_time(ev[1]))
+    del d_wr, lg
     flops = 6.0 * T * k * H * I + (6.0 * T * H * I if wl.n_shared else 0.0)
     tflops = flops / (gms / 1e3) / 1e12
     nb = B.moe_expert_bytes(cfg)
     del g
     res = {"tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_chunk": round(ms, 4), "tokens": T,
            "gemm_ms": round(gms, 4), "gemm_tflops": round(tflops, 1),
+           "router_logits_ms": round(float(np.median(rl_ms)), 4),
            "mfma_frac_bf16_peak": round(tflops / 2500.0, 4), "gflop": round(flops / 1e9, 1),
            "pool_gb": round(nb * E / 1e9, 3), "weights": wl.wdtype,
            "note": "layer pool resident in HBM; MXFP4 weights dequantised to bf16 MFMA inputs"}

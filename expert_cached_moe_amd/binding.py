@@ -34,7 +34,7 @@ EXPORTS = [
     "moe_workspace_bytes", "moe_pair_rows", "moe_pack_expert", "moe_bind_pools", "moe_route",
     "moe_qstar", "moe_lru_step", "moe_lru_replay", "moe_lru_reset", "moe_lru_slots", "moe_lru_stats",
     "moe_fill", "moe_fill_wait", "moe_upload", "moe_expert_ffn", "moe_host_ffn", "moe_merge_partial",
-    "moe_prefill_stream",
+    "moe_prefill_stream", "moe_router_logits",
 ]
 
 
@@ -69,6 +69,7 @@ _sig = {
     "moe_pack_expert": (ctypes.c_int, [_P(moe_config), vp, vp, vp, vp, vp, vp, vp]),
     "moe_bind_pools": (ctypes.c_int, [vp, vp, ctypes.c_int32, vp, ctypes.c_int32]),
     "moe_route": (ctypes.c_int, [vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp]),
+    "moe_router_logits": (ctypes.c_int, [vp, vp, ctypes.c_int32, vp, vp, vp]),
     "moe_qstar": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_double, ctypes.c_double, ctypes.c_int32]),
     "moe_lru_step": (ctypes.c_int, [vp, ctypes.c_int32, vp, ctypes.c_int32, _P(moe_plan)]),
     "moe_lru_replay": (ctypes.c_int, [vp, ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32, vp, _P(moe_stats)]),
@@ -182,6 +183,10 @@ def moe_pack_expert(cfg, wg, wu, wd, sg, su, sd, blob) -> None:
 
 def moe_bind_pools(ctx, d_slots, n_slots, h_pool, n_pool) -> None:
     _check(ctx, _lib.moe_bind_pools(ctx, _ptr(d_slots), n_slots, _ptr(h_pool), n_pool))
+
+
+def moe_router_logits(ctx, d_x, T, d_wr, d_logits, s=None) -> None:
+    _check(ctx, _lib.moe_router_logits(ctx, _ptr(d_x), T, _ptr(d_wr), _ptr(d_logits), _stream(s)))
 
 
 def moe_route(ctx, d_logits, T, d_topk_ids, d_topk_w, d_counts, d_offsets, d_perm, d_inv, d_ws, s=None) -> None:

@@ -203,6 +203,15 @@ int moe_bind_pools(moe_ctx* ctx, void* d_slots, int32_t n_slots, const void* h_p
     return MOE_OK;
 }
 
+int moe_router_logits(moe_ctx* ctx, const void* d_x, int32_t T, const float* d_wr, float* d_logits, hipStream_t s) {
+    if (!ctx) return MOE_EINVAL;
+    if (T < 0) return fail(ctx, MOE_EINVAL, "T < 0");
+    if (T == 0) return MOE_OK;
+    if (!d_x || !d_wr || !d_logits) return fail(ctx, MOE_EINVAL, "null router buffer");
+    hipError_t e = launch_router_logits(ctx->cfg, d_x, T, d_wr, d_logits, s);
+    return e == hipSuccess ? MOE_OK : hip_fail(ctx, e, "moe_router_logits launch");
+}
+
 int moe_route(moe_ctx* ctx, const float* d_logits, int32_t T, int32_t* d_topk_ids, float* d_topk_w,
               int32_t* d_counts, int32_t* d_offsets, int32_t* d_perm, int32_t* d_inv, void* d_ws,
               hipStream_t s) {

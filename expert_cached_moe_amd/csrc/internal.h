@@ -139,6 +139,8 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
                            hipStream_t s);
 bool gemm_shape_supported(const moe_config& c);
 
+hipError_t launch_router_logits(const moe_config& c, const void* x, int32_t T, const float* wr, float* out,
+                                hipStream_t s);
 hipError_t launch_merge(const moe_config& c, const float* o, const int32_t* ids, const float* w,
                         const uint32_t* gpu_mask, int32_t with_shared, const float* y_host,
                         int32_t T, void* out, hipStream_t s);

@@ -154,6 +154,13 @@ int moe_pack_expert(const moe_config* cfg, const void* wg, const void* wu, const
 int moe_bind_pools(moe_ctx* ctx, void* d_slots, int32_t n_slots, const void* h_pool, int32_t n_pool);
 
 /* ---------------------------------------------------------------- router */
+/* Router logits of T tokens (async on s): d_logits[t][e] = sum_h d_x[t][h] * d_wr[e][h],
+ * accumulated in fp32.  d_x [T][H] in the activation dtype (fp32 for fp32 weights, else
+ * bf16); d_wr [E][H] fp32, one contiguous row of router weights per expert; d_logits [T][E]
+ * fp32 (the input of moe_route).  T == 0 is a valid no-op.  ([B] "Sparsity Is a Lie": a
+ * small router scores the experts of each token.) */
+int moe_router_logits(moe_ctx* ctx, const void* d_x, int32_t T, const float* d_wr, float* d_logits,
+                      hipStream_t s);
 /* Softmax + top-k and token-by-expert permutation of T tokens (async on s).
  *   d_logits [T][E] fp32 (finite; NaN order is unspecified);
  *   d_topk_ids [T][k] int32 (logit descending, lower id first on equal logits);
