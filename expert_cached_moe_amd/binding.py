@@ -34,8 +34,14 @@ EXPORTS = [
     "moe_workspace_bytes", "moe_pair_rows", "moe_pack_expert", "moe_bind_pools", "moe_route",
     "moe_qstar", "moe_lru_step", "moe_lru_replay", "moe_lru_reset", "moe_lru_slots", "moe_lru_stats",
     "moe_fill", "moe_fill_wait", "moe_upload", "moe_expert_ffn", "moe_host_ffn", "moe_merge_partial",
-    "moe_prefill_stream", "moe_router_logits",
+    "moe_prefill_stream", "moe_router_logits", "moe_lru_resize", "moe_move_slots",
 ]
+
+
+class moe_resize(ctypes.Structure):
+    _fields_ = [("cap", ctypes.c_int32), ("n_move", ctypes.c_int32), ("n_evict", ctypes.c_int32),
+                ("move_src", ctypes.POINTER(ctypes.c_int32)), ("move_dst", ctypes.POINTER(ctypes.c_int32)),
+                ("evicted", ctypes.POINTER(ctypes.c_int32))]
 
 
 class moe_config(ctypes.Structure):
@@ -76,6 +82,8 @@ _sig = {
     "moe_lru_reset": (ctypes.c_int, [vp]),
     "moe_lru_slots": (ctypes.c_int, [vp, ctypes.c_int32, vp]),
     "moe_lru_stats": (ctypes.c_int, [vp, _P(moe_stats)]),
+    "moe_lru_resize": (ctypes.c_int, [vp, ctypes.c_int32, _P(moe_resize)]),
+    "moe_move_slots": (ctypes.c_int, [vp, _P(moe_resize), vp]),
     "moe_fill": (ctypes.c_int, [vp, _P(moe_plan), vp]),
     "moe_fill_wait": (ctypes.c_int, [vp, vp]),
     "moe_upload": (ctypes.c_int, [vp, vp, vp, ctypes.c_int64, vp]),
@@ -250,6 +258,31 @@ def moe_lru_stats(ctx) -> moe_stats:
     st = moe_stats()
     _check(ctx, _lib.moe_lru_stats(ctx, ctypes.byref(st)))
     return st
+
+
+class Resize:
+    """Host arrays of a cache resize and the moe_resize struct pointing at them."""
+
+    def __init__(self, cap: int):
+        self.arrays = {f: np.zeros(max(cap, 1), np.int32) for f in ("move_src", "move_dst", "evicted")}
+        c_i32p = ctypes.POINTER(ctypes.c_int32)
+        self.c = moe_resize(cap, 0, 0, *[self.arrays[f].ctypes.data_as(c_i32p) for f in ("move_src", "move_dst",
+                                                                                         "evicted")])
+
+    def moves(self):
+        n = self.c.n_move
+        return list(zip(self.arrays["move_src"][:n].tolist(), self.arrays["move_dst"][:n].tolist()))
+
+    def evicted(self):
+        return self.arrays["evicted"][: self.c.n_evict].tolist()
+
+
+def moe_lru_resize(ctx, new_slots, r: Resize) -> None:
+    _check(ctx, _lib.moe_lru_resize(ctx, new_slots, ctypes.byref(r.c)))
+
+
+def moe_move_slots(ctx, r: Resize, s=None) -> None:
+    _check(ctx, _lib.moe_move_slots(ctx, ctypes.byref(r.c), _stream(s)))
 
 
 def moe_fill(ctx, plan: Plan, side=None) -> None:

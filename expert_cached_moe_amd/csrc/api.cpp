@@ -270,6 +270,24 @@ int moe_upload(moe_ctx* ctx, void* d_dst, const void* h_src, int64_t bytes, hipS
     return e == hipSuccess ? MOE_OK : hip_fail(ctx, e, "hipEventRecord (upload)");
 }
 
+int moe_move_slots(moe_ctx* ctx, const moe_resize* r, hipStream_t s) {
+    if (!ctx || !r) return MOE_EINVAL;
+    if (r->n_move < 0 || (r->n_move > 0 && (!r->move_src || !r->move_dst))) return fail(ctx, MOE_EINVAL, "bad resize");
+    if (r->n_move > 0 && !ctx->d_slots) return fail(ctx, MOE_ESTATE, "moe_move_slots needs a bound device pool");
+    for (int i = 0; i < r->n_move; ++i)
+        if (r->move_src[i] < 0 || r->move_src[i] >= ctx->n_bound_slots || r->move_dst[i] < 0 ||
+            r->move_dst[i] >= ctx->n_bound_slots || r->move_src[i] == r->move_dst[i])
+            return fail(ctx, MOE_EINVAL, "move outside the bound device pool");
+    const int64_t bytes = ctx->lay.bytes;
+    uint8_t* base = static_cast<uint8_t*>(ctx->d_slots);
+    for (int i = 0; i < r->n_move; ++i) {
+        hipError_t e = hipMemcpyAsync(base + int64_t(r->move_dst[i]) * bytes, base + int64_t(r->move_src[i]) * bytes,
+                                      bytes, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return hip_fail(ctx, e, "hipMemcpyAsync (slot move)");
+    }
+    return MOE_OK;
+}
+
 int moe_fill_wait(moe_ctx* ctx, hipStream_t s) {
     if (!ctx) return MOE_EINVAL;
     if (!ctx->fill_event) return MOE_OK;  // nothing was ever filled

@@ -210,6 +210,67 @@ int moe_lru_slots(const moe_ctx* ctx, int32_t layer, int32_t* h_slot_of_expert) 
     return MOE_OK;
 }
 
+int moe_lru_resize(moe_ctx* ctx, int32_t new_slots, moe_resize* out) {
+    if (!ctx || !out) return MOE_EINVAL;
+    if (new_slots < 0 || new_slots > (1 << 21)) return fail(ctx, MOE_EINVAL, "new_slots out of range");
+    const int C = ctx->cfg.n_slots;
+    std::vector<int32_t> moves_src, moves_dst, evicted;
+    std::vector<char> keep(size_t(C), 0);
+    if (new_slots < C) {
+        std::vector<int32_t> resident;
+        for (int s = 0; s < C; ++s)
+            if (ctx->key_of_slot[s] >= 0) resident.push_back(s);
+        std::vector<int32_t> by_recency = resident;
+        std::sort(by_recency.begin(), by_recency.end(),
+                  [&](int32_t a, int32_t b) { return ctx->recency[a] > ctx->recency[b]; });
+        const size_t n_keep = std::min(by_recency.size(), size_t(new_slots));
+        for (size_t i = 0; i < n_keep; ++i) keep[by_recency[i]] = 1;
+        for (int32_t s : resident)
+            if (!keep[s]) evicted.push_back(ctx->key_of_slot[s]);
+        int32_t next_free = 0;
+        for (int s = new_slots; s < C; ++s) {
+            if (!keep[s]) continue;
+            while (keep[next_free]) ++next_free;   // a free slot below new_slots exists: kept <= new_slots
+            moves_src.push_back(s);
+            moves_dst.push_back(next_free);
+            ++next_free;
+        }
+    }
+    if (out->cap < int32_t(moves_src.size()) || out->cap < int32_t(evicted.size()))
+        return fail(ctx, MOE_ECAPACITY, "resize arrays below the moves or evictions");
+    if ((!moves_src.empty() && (!out->move_src || !out->move_dst)) || (!evicted.empty() && !out->evicted))
+        return fail(ctx, MOE_EINVAL, "null resize array");
+
+    // ---- mutate (all checks are done) ----
+    if (new_slots < C) {
+        for (int32_t key : evicted) {
+            const int32_t s = ctx->slot_of_key[key];
+            ctx->slot_of_key[key] = -1;
+            ctx->key_of_slot[s] = -1;
+            ctx->recency[s] = 0;
+        }
+        for (size_t i = 0; i < moves_src.size(); ++i) {
+            const int32_t a = moves_src[i], b = moves_dst[i], key = ctx->key_of_slot[a];
+            ctx->key_of_slot[b] = key;
+            ctx->recency[b] = ctx->recency[a];
+            ctx->slot_of_key[key] = b;
+            ctx->key_of_slot[a] = -1;
+            ctx->recency[a] = 0;
+        }
+    }
+    ctx->key_of_slot.resize(size_t(new_slots), -1);
+    ctx->recency.resize(size_t(new_slots), 0);
+    ctx->cfg.n_slots = new_slots;   // the bound device pool stays bound (moves run in it) until rebound
+    out->n_move = int32_t(moves_src.size());
+    out->n_evict = int32_t(evicted.size());
+    if (!moves_src.empty()) {
+        std::memcpy(out->move_src, moves_src.data(), moves_src.size() * 4);
+        std::memcpy(out->move_dst, moves_dst.data(), moves_dst.size() * 4);
+    }
+    if (!evicted.empty()) std::memcpy(out->evicted, evicted.data(), evicted.size() * 4);
+    return MOE_OK;
+}
+
 int moe_lru_stats(const moe_ctx* ctx, moe_stats* stats) {
     if (!ctx || !stats) return MOE_EINVAL;
     *stats = ctx->stats;

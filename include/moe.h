@@ -110,6 +110,16 @@ typedef struct moe_stats {
     int64_t evictions;
 } moe_stats;
 
+/* Result of a cache resize (moe_lru_resize); arrays are caller-owned with capacity cap. */
+typedef struct moe_resize {
+    int32_t cap;        /* capacity of each array */
+    int32_t n_move;     /* kept entries that leave a slot past the new size */
+    int32_t n_evict;    /* entries dropped by a shrink */
+    int32_t* move_src;  /* [cap] slot an entry leaves (>= new size) */
+    int32_t* move_dst;  /* [cap] free slot below the new size it moves to */
+    int32_t* evicted;   /* [cap] cache keys (layer*E + expert) dropped, in slot order */
+} moe_resize;
+
 typedef struct moe_ctx moe_ctx;
 
 /* ---------------------------------------------------------------- context */
@@ -190,6 +200,19 @@ int moe_lru_replay(moe_ctx* ctx, int32_t layer, const int32_t* h_topk_ids, int32
 int moe_lru_reset(moe_ctx* ctx);
 /* This layer's current slot table (h_slot_of_expert [E], -1 = absent). */
 int moe_lru_slots(const moe_ctx* ctx, int32_t layer, int32_t* h_slot_of_expert);
+/* Elastic slot pool ([B] "Elastic Memory": at a scheduler safe point the GPU expert
+ * cache is rebuilt under a new VRAM budget without reloading the host pool).  Host only,
+ * between steps.  Shrink (new_slots < current): the new_slots most recently used entries
+ * stay, the others are evicted; kept entries in slots >= new_slots move to the lowest free
+ * slots below new_slots (in ascending source-slot order).  Grow: every entry stays and
+ * slots are added free.  The returned moves are applied to the device pool with
+ * moe_move_slots before the pool is rebound at the new size (moe_bind_pools).  0 <=
+ * new_slots <= 2^21.  Errors (no state change): MOE_EINVAL, MOE_ECAPACITY (cap below the
+ * moves or evictions). */
+int moe_lru_resize(moe_ctx* ctx, int32_t new_slots, moe_resize* out);
+/* Copy every move of a resize inside the bound device slot pool (device to device, async
+ * on s).  Every source and destination must lie in the bound pool. */
+int moe_move_slots(moe_ctx* ctx, const moe_resize* r, hipStream_t s);
 /* Cumulative statistics since create/reset. */
 int moe_lru_stats(const moe_ctx* ctx, moe_stats* stats);
 

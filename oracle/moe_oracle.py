@@ -306,6 +306,36 @@ class LRUCache:
                 "fill_slot": fill_slot, "fill_victim": fill_victim, "host": host,
                 "m": m, "q": q, "slot_of_expert": self.slot_table(layer)}
 
+    def resize(self, new_C: int) -> dict:
+        """Rebuild the cache under a new slot count at a safe point, keeping the host pool
+        ([B] "Elastic Memory").  Shrinking keeps the new_C most recently used entries and
+        drops the rest; a kept entry whose slot no longer exists takes the lowest free slot
+        (sources in ascending slot order).  Growing keeps every entry and adds free slots."""
+        new_C = int(new_C)
+        moves, evicted = [], []
+        if new_C < self.C:
+            resident = [s for s in range(self.C) if self.key_of_slot[s] >= 0]
+            newest_first = sorted(resident, key=lambda s: self.recency[s], reverse=True)
+            kept = set(newest_first[:new_C])
+            evicted = [self.key_of_slot[s] for s in resident if s not in kept]
+            for s in resident:
+                if s not in kept:
+                    self.key_of_slot[s] = -1
+                    self.recency[s] = None
+            free = [s for s in range(new_C) if s not in kept]
+            for src in sorted(s for s in kept if s >= new_C):
+                dst = free.pop(0)
+                self.key_of_slot[dst], self.recency[dst] = self.key_of_slot[src], self.recency[src]
+                self.key_of_slot[src], self.recency[src] = -1, None
+                moves.append((src, dst))
+            self.key_of_slot = self.key_of_slot[:new_C]
+            self.recency = self.recency[:new_C]
+        else:
+            self.key_of_slot += [-1] * (new_C - self.C)
+            self.recency += [None] * (new_C - self.C)
+        self.C = new_C
+        return {"moves": moves, "evicted": evicted}
+
 
 def mattson_misses(step_sets, max_C: int) -> np.ndarray:
     """Stack-distance pass (Mattson et al., 1970): misses of an LRU cache of every

@@ -179,6 +179,61 @@ def test_planner_errors_leave_state_untouched():
     B.moe_destroy(ctx)
 
 
+@pytest.mark.parametrize("bp,bh", [(52.7, 77.3), (1.0, 1.0)])
+def test_planner_resize_matches_oracle(bp, bh):
+    """C++ planner vs the oracle with resizes at random safe points (shrinks, grows, down to
+    zero slots): every plan, every move and eviction list, and the slot tables bit-exact."""
+    wl = synth.workload("a3b_decode_bf16")
+    Bt, n = 4, 400
+    logits, _ = synth.zipf_reuse_trace(wl, Bt, n)
+    ids_steps = [oracle.route(logits[t], wl.k)[0] for t in range(n)]
+    rng = np.random.default_rng(5)
+    events = {int(t): int(c) for t, c in zip(rng.choice(n, 12, replace=False), rng.integers(0, 80, 12))}
+    events[200] = 0
+    cfg = config(wl, n_slots=wl.C, bp=bp, bh=bh)
+    ctx = B.moe_create(cfg)
+    try:
+        ref = oracle.LRUCache(wl.C, wl.E)
+        plan = B.Plan(min(wl.E, Bt * wl.k), wl.E)
+        for t in range(n):
+            if t in events:
+                r = B.Resize(128)
+                B.moe_lru_resize(ctx, events[t], r)
+                want = ref.resize(events[t])
+                assert r.moves() == want["moves"] and r.evicted() == want["evicted"], t
+                assert np.array_equal(B.moe_lru_slots(ctx, 0, wl.E), ref.slot_table(0)), t
+            B.moe_lru_step(ctx, 0, ids_steps[t], Bt, plan)
+            want = ref.step(ids_steps[t], bp, bh)
+            got = _plan_dict(plan)
+            for key in got:
+                assert got[key] == want[key], (t, key)
+            assert np.array_equal(plan.get("slot_of_expert"), want["slot_of_expert"]), t
+    finally:
+        B.moe_destroy(ctx)
+
+
+def test_resize_errors_leave_state_untouched():
+    wl = synth.workload("tiny_fp32")
+    ctx = B.moe_create(config(wl, n_slots=4, bp=1.0, bh=1.0))
+    try:
+        plan = B.Plan(2, wl.E)
+        for ids in ([0, 1], [2, 3], [4, 5], [1, 6]):
+            B.moe_lru_step(ctx, 0, np.array([ids], np.int32), 1, plan)
+        before = B.moe_lru_slots(ctx, 0, wl.E).copy()
+        with pytest.raises(B.MoeError):
+            B.moe_lru_resize(ctx, -1, B.Resize(8))
+        with pytest.raises(B.MoeError):
+            B.moe_lru_resize(ctx, 2, B.Resize(1))          # two moves and two evictions
+        assert np.array_equal(B.moe_lru_slots(ctx, 0, wl.E), before)
+        r = B.Resize(2)
+        B.moe_lru_resize(ctx, 2, r)
+        assert r.moves() == [(2, 0), (3, 1)] and r.evicted() == [5, 4]
+        with pytest.raises(B.MoeError):                   # a pool larger than the resized cache is refused
+            B.moe_bind_pools(ctx, 1, 3, None, 0)
+    finally:
+        B.moe_destroy(ctx)
+
+
 def test_multilayer_keys():
     """Two layers share one cache; keys are (layer, expert)."""
     wl = synth.workload("tiny_fp32")

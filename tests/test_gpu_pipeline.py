@@ -51,8 +51,19 @@ def _decode_inputs(wl, Bt, n_steps):
                                              ("a3b_decode_bf16", 1, 32), ("v4flash_decode_bf16", 1, 6),
                                              ("v4flash_mxfp4", 2, 6)])
 def test_cached_decode_pipeline(B, name, Bt, n_steps):
+    _run_pipeline(B, name, Bt, n_steps)
+
+
+def test_cached_decode_pipeline_resize(B):
+    """Elastic slot pool under the pipeline ([B] "Elastic Memory"): shrink 47 -> 20 slots
+    before step 8 (moves copied inside the device pool, freed slots poisoned, pool rebound
+    smaller), grow back to 47 before step 16 (the new slots are poisoned until filled)."""
+    _run_pipeline(B, "a3b_decode_bf16", 4, 24, resizes={8: 20, 16: 47})
+
+
+def _run_pipeline(B, name, Bt, n_steps, resizes=None):
     from expert_cached_moe_amd.runtime import LayerBuffers, pack_pool
-    print(f"[pipeline] {name} B={Bt} steps={n_steps}", flush=True)
+    print(f"[pipeline] {name} B={Bt} steps={n_steps} resizes={resizes}", flush=True)
     wl = synth.workload(name)
     E, k, H = wl.E, wl.k, wl.H
     logits, x = _decode_inputs(wl, Bt, n_steps)
@@ -78,7 +89,19 @@ def test_cached_decode_pipeline(B, name, Bt, n_steps):
     main, side = torch.cuda.current_stream(), torch.cuda.Stream()
     xf = oracle.act_f64(x, wl.act_dtype)
     worst, n_host, n_fill = 0.0, 0, 0
+    C = wl.C
     for s in range(n_steps):
+        if resizes and s in resizes:
+            newC = resizes[s]
+            r = B.Resize(256)
+            B.moe_lru_resize(L.ctx, newC, r)
+            want_r = ref_cache.resize(newC)
+            assert r.moves() == want_r["moves"] and r.evicted() == want_r["evicted"], s
+            B.moe_move_slots(L.ctx, r, main)
+            if newC < C:
+                slots[newC * nb:C * nb].fill_(0xFF)          # freed slots: any later read shows up as NaN
+            B.moe_bind_pools(L.ctx, slots, newC, host_pool, E)
+            C = newC
         L.route(d_logits[s * Bt:(s + 1) * Bt], Bt, main)
         ids = L.ids[: Bt * k].cpu().numpy().reshape(Bt, k)          # synchronises the route
         gates = L.w[: Bt * k].cpu().numpy().reshape(Bt, k)
@@ -110,6 +133,7 @@ def test_cached_decode_pipeline(B, name, Bt, n_steps):
         n_host += len(want["host"])
         n_fill += len(want["fill"])
     print(f"[pipeline] {name}: worst rel err {worst:.2e}, fills {n_fill}, host experts {n_host}", flush=True)
+    assert np.array_equal(B.moe_lru_slots(L.ctx, 0, E), ref_cache.slot_table(0))
     assert n_fill > 0
     L.close()
 

@@ -326,6 +326,60 @@ def test_lru_plan_invariants():
             assert all(tab[e] < 0 for e in p["host"])
 
 
+def test_resize_hand_case():
+    """Hand-derived ([B] "Elastic Memory" reading: keep the most recent, move survivors down).
+    C = 4, every miss filled.  Steps {0,1}, {2,3}: slots 0..3 = e0, e1, e2, e3 with recency
+    (1,2) (1,1) (2,2) (2,1).  Step {4,5}: victims e1 (1,1) then e0 (1,2): slot 1 = e4 (3,2),
+    slot 0 = e5 (3,1).  Step {1,6}: victims e3 (2,1), e2 (2,2): slot 3 = e1 (4,2), slot 2 =
+    e6 (4,1).  Shrink to 2: keep e1, e6 (the two most recent), drop e5 (slot 0) and e4
+    (slot 1), move slot 2 -> 0 and slot 3 -> 1."""
+    c = oracle.LRUCache(4, 8)
+    for ids in ([0, 1], [2, 3], [4, 5], [1, 6]):
+        c.step(np.array([ids]), 1.0, 1.0)
+    assert c.slot_table().tolist() == [-1, 3, -1, -1, 1, 0, 2, -1]
+    r = c.resize(2)
+    assert r == {"moves": [(2, 0), (3, 1)], "evicted": [5, 4]}
+    assert c.slot_table().tolist() == [-1, 1, -1, -1, -1, -1, 0, -1]
+    # the next step hits e6 and e1 in their new slots; a miss now evicts the older of the two
+    p = c.step(np.array([[6, 7]]), 1.0, 1.0)
+    assert (p["hit"], p["hit_slot"], p["fill"], p["fill_slot"], p["fill_victim"]) == ([6], [0], [7], [1], [1])
+
+
+@pytest.mark.parametrize("E,k,B,C,C2", [(16, 2, 1, 8, 3), (24, 3, 1, 12, 5), (20, 2, 2, 10, 6), (12, 1, 3, 9, 4)])
+def test_resize_shrink_equals_smaller_cache(E, k, B, C, C2):
+    """With every miss filled the cache is a stack algorithm: a cache of size C shrunk to C2
+    at any step holds exactly the C2 most recent keys, which is what a cache that had size
+    C2 all along holds, so from then on both take the same hits and misses."""
+    rng = np.random.default_rng(E + 7 * C + C2)
+    pz = 1.0 / np.arange(1, E + 1) ** 1.1
+    steps = [np.stack([rng.choice(E, size=k, replace=False, p=pz / pz.sum()) for _ in range(B)])
+             for _ in range(120)]
+    assert max(len(oracle.step_order(s)) for s in steps) <= C2
+    for cut in (0, 1, 17, 60, 119):
+        big, small = oracle.LRUCache(C, E), oracle.LRUCache(C2, E)
+        for t, s in enumerate(steps):
+            if t == cut:
+                big.resize(C2)
+                keys_big = sorted(x for x in big.key_of_slot if x >= 0)
+                keys_small = sorted(x for x in small.key_of_slot if x >= 0)
+                assert keys_big == keys_small, (cut, keys_big, keys_small)
+            pb, ps = big.step(s, 1.0, 1.0), small.step(s, 1.0, 1.0)
+            if t >= cut:
+                assert sorted(pb["hit"]) == sorted(ps["hit"]) and sorted(pb["fill"]) == sorted(ps["fill"]), (cut, t)
+
+
+def test_resize_grow_then_shrink_back_is_identity():
+    wl = synth.workload("a3b_decode_bf16")
+    logits, _ = synth.zipf_reuse_trace(wl, 4, 60)
+    c = oracle.LRUCache(wl.C, wl.E)
+    for t in range(60):
+        c.step(oracle.route(logits[t], wl.k)[0], 52.7, 77.3)
+    before = (list(c.key_of_slot), list(c.recency))
+    assert c.resize(wl.C + 30) == {"moves": [], "evicted": []}
+    assert c.resize(wl.C) == {"moves": [], "evicted": []}
+    assert (c.key_of_slot, c.recency) == before
+
+
 # ------------------------------------------------------------------ MXFP4
 def test_mxfp4_table_and_packing():
     table = {int(c): float(v) for c, v in (ln.split() for ln in _lines("mxfp4_codes.txt"))}
