@@ -465,19 +465,98 @@ def stream_chunk(args, wl, cfg, host_pool, shared, d_logits, d_x, L, compute_ms)
             "note": "PCIe-inclusive; prediction: double = U + (n-1) max(U, C) + C, single = n (U + C)"}
 
 
+def measure_bandwidths(B, ctx, host_pool, slots, nb, wl, side, n_exp=16):
+    """The pages' two rates on this machine: B_P, pinned host -> device copies of single
+    expert blobs (as fills are issued), and B_H, the rate at which the CPU experts
+    (moe_host_ffn) stream expert weights from the pinned pool, at 6 threads (the pages'
+    setting) and at all threads."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_exp = min(n_exp, wl.E, wl.C)
+
+    def timed(per_blob):
+        ts = []
+        for rep in range(6):                              # the first pass warms the path up
+            e0.record(side)
+            if per_blob:
+                for i in range(n_exp):
+                    B.moe_upload(ctx, slots[i * nb:(i + 1) * nb], host_pool[i * nb:(i + 1) * nb], nb, side)
+            else:
+                B.moe_upload(ctx, slots[: n_exp * nb], host_pool[: n_exp * nb], n_exp * nb, side)
+            e1.record(side)
+            torch.cuda.synchronize()
+            if rep:
+                ts.append(e0.elapsed_time(e1))
+        return n_exp * nb / (float(np.median(ts)) / 1e3) / 1e9
+
+    bp = timed(True)
+    bp_batched = timed(False)
+    k = wl.k
+    T = (n_exp + k - 1) // k
+    ids = np.array([[(t * k + j) % n_exp if t * k + j < n_exp else (t * k + j) % wl.E for j in range(k)]
+                    for t in range(T)], np.int32)
+    host = sorted(set(ids.ravel().tolist()))
+    plan = B.Plan(len(host), wl.E)
+    plan.arrays["host"][: len(host)] = host
+    plan.c.n_host = len(host)
+    plan.c.layer = 0
+    h_x = torch.zeros(T * wl.H, dtype=torch.int16 if wl.act_dtype == "bf16" else torch.float32)
+    h_w = np.full((T, k), 1.0 / k, np.float32)
+    h_y = torch.zeros(T * wl.H, dtype=torch.float32)
+    out = {}
+    for label, nt in (("bh_gbps_6_threads", 6), ("bh_gbps_all_threads", os.cpu_count() or 1)):
+        ts = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            B.moe_host_ffn(ctx, h_x, T, ids, h_w, plan, h_y, nt)
+            ts.append(time.perf_counter() - t0)
+        out[label] = round(len(host) * payload_bytes(wl) / float(np.median(ts)) / 1e9, 2)
+    nt = min(16, os.cpu_count() or 1)
+    ts = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        B.moe_host_ffn(ctx, h_x, T, ids, h_w, plan, h_y, nt)
+        ts.append(time.perf_counter() - t0)
+    out["bh_gbps_pipeline_threads"] = round(len(host) * payload_bytes(wl) / float(np.median(ts)) / 1e9, 2)
+    out = {"bp_gbps": round(bp, 2), "bp_gbps_one_copy": round(bp_batched, 2), **out,
+           "threads_all": os.cpu_count() or 1, "threads_pipeline": nt}
+    bh = out["bh_gbps_pipeline_threads"]
+    out["qstar_at_measured_ratio"] = {m: B.moe_qstar(m, bp, bh, 0) for m in range(1, 9)}
+    return out
+
+
 def pipeline(args, wl, experts, logits, x, dt):
     """Cached decode: route on the GPU, plan on the host (global LRU + q*), upload the
-    fills on a side stream while the hits run, CPU experts in parallel, merge."""
+    fills on a side stream while the hits run, CPU experts in parallel, merge.  Run at the
+    pages' B_P:B_H and at the ratio measured on this machine (per-blob fills, and the CPU
+    experts at the pipeline's own thread count)."""
     import torch
     from expert_cached_moe_amd import binding as B
-    from expert_cached_moe_amd.runtime import LayerBuffers, pack_pool
-    Bt, E, k, H = args.batch, wl.E, wl.k, wl.H
-    cfg = B.make_config(wl.H, wl.I, E, k, wl.n_shared, wl.C, 1, dt, 1, 0, 52.7, 77.3)
-    L = LayerBuffers(cfg, Bt)
-    nb = B.moe_expert_bytes(cfg)
-    host_pool = pack_pool(cfg, [experts[e] for e in range(E)], pin=True)
+    from expert_cached_moe_amd.runtime import pack_pool
+    E = wl.E
+    cfg0 = B.make_config(wl.H, wl.I, E, wl.k, wl.n_shared, wl.C, 1, dt, 1, 0, 52.7, 77.3)
+    nb = B.moe_expert_bytes(cfg0)
+    host_pool = pack_pool(cfg0, [experts[e] for e in range(E)], pin=True)
     slots = torch.empty(wl.C * nb, dtype=torch.uint8, device="cuda")
-    shared = pack_pool(cfg, [experts[E]], pin=False).cuda() if wl.n_shared else None
+    shared = pack_pool(cfg0, [experts[E]], pin=False).cuda() if wl.n_shared else None
+    ctx0 = B.moe_create(cfg0)
+    B.moe_bind_pools(ctx0, slots, wl.C, host_pool, E)
+    bw = measure_bandwidths(B, ctx0, host_pool, slots, nb, wl, torch.cuda.Stream())
+    B.moe_destroy(ctx0)
+    res = run_pipeline(args, wl, logits, x, dt, host_pool, slots, shared, 52.7, 77.3)
+    res["measured"] = bw
+    res["at_measured_ratio"] = run_pipeline(args, wl, logits, x, dt, host_pool, slots, shared, bw["bp_gbps"],
+                                            bw["bh_gbps_pipeline_threads"])
+    return res
+
+
+def run_pipeline(args, wl, logits, x, dt, host_pool, slots, shared, bp, bh):
+    import torch
+    from expert_cached_moe_amd import binding as B
+    from expert_cached_moe_amd.runtime import LayerBuffers
+    Bt, E, k, H = args.batch, wl.E, wl.k, wl.H
+    cfg = B.make_config(wl.H, wl.I, E, k, wl.n_shared, wl.C, 1, dt, 1, 0, bp, bh)
+    L = LayerBuffers(cfg, Bt)
     B.moe_bind_pools(L.ctx, slots, wl.C, host_pool, E)
     n_trace = wl.steps
     d_logits = torch.from_numpy(logits.reshape(n_trace * Bt, E)).cuda()
@@ -529,7 +608,7 @@ def pipeline(args, wl, experts, logits, x, dt):
     st = B.moe_lru_stats(L.ctx)
     L.close()
     return {"tokens_per_s": round(Bt * n / dt_s, 1), "steps": n, "ms_per_step": round(dt_s * 1e3 / n, 4),
-            "slots": wl.C, "bp_bh": [52.7, 77.3], "miss_rate": round(st.misses / max(1, st.distinct), 4),
+            "slots": wl.C, "bp_bh": [bp, bh], "miss_rate": round(st.misses / max(1, st.distinct), 4),
             "fills_per_step": round(st.fills / n, 3), "host_experts_per_step": round(st.host / n, 3),
             "cold_start": True, "note": "includes host-link fills and CPU experts; context only"}
 
