@@ -298,7 +298,8 @@ def decode(args, wl, Bt, experts):
     ffn_bytes = 0.0
     for s in range(n_prof):
         ne = len(step_experts[(W + s) % n_trace])
-        ffn_bytes += (ne + with_shared) * payload_bytes(wl) + Bt * H * (2 if wl.act_dtype == "bf16" else 4) + pairs * H * 4
+        act = 2 if wl.act_dtype == "bf16" else 4
+        ffn_bytes += (ne + with_shared) * payload_bytes(wl) + Bt * H * act + pairs * H * act
     ffn_bytes /= n_prof
     achieved = ffn_bytes / (ffn_ms / 1e3) / 1e9
     rec = TRAFFIC.get((wl.name, Bt))

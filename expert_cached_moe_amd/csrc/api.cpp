@@ -297,7 +297,7 @@ int moe_fill_wait(moe_ctx* ctx, hipStream_t s) {
 
 int moe_expert_ffn(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* h_topk_ids, const int32_t* d_offsets,
                    const int32_t* d_perm, const void* d_slot_base, const int32_t* h_experts, const int32_t* h_slots,
-                   int32_t n, const void* d_shared, int32_t with_shared, float* d_o, void* d_ws, hipStream_t s) {
+                   int32_t n, const void* d_shared, int32_t with_shared, void* d_o, void* d_ws, hipStream_t s) {
     if (!ctx) return MOE_EINVAL;
     const moe_config& c = ctx->cfg;
     if (T < 0) return fail(ctx, MOE_EINVAL, "T < 0");
@@ -357,7 +357,7 @@ int moe_expert_ffn(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* h_to
     return e == hipSuccess ? MOE_OK : hip_fail(ctx, e, "moe_expert_ffn launch");
 }
 
-int moe_merge_partial(moe_ctx* ctx, const float* d_o, const int32_t* d_topk_ids, const float* d_topk_w,
+int moe_merge_partial(moe_ctx* ctx, const void* d_o, const int32_t* d_topk_ids, const float* d_topk_w,
                       const int32_t* h_gpu_experts, int32_t n_gpu, int32_t with_shared, const float* d_y_host,
                       int32_t T, void* d_out, hipStream_t s) {
     if (!ctx) return MOE_EINVAL;

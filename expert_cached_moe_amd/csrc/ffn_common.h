@@ -100,7 +100,8 @@ __device__ __forceinline__ uint4 load_w(const uint8_t* row, int ch) {
 }
 
 template <int WT>
-__device__ __forceinline__ void store_h(uint8_t* h, int64_t idx, float v) {
+// Store in the activation dtype (fp32 for fp32 weights, bf16 otherwise): h and pair outputs.
+__device__ __forceinline__ void store_act(uint8_t* h, int64_t idx, float v) {
     if (WT == WT_F32)
         reinterpret_cast<float*>(h)[idx] = v;
     else

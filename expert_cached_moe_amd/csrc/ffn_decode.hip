@@ -109,7 +109,7 @@ __global__ void __launch_bounds__(64 * GateUpShape<CPL>::WPB) k_decode_gate_up(c
         const int qi = dev::group_reduce_split<RPW, 64>(part, lane);
         const float up = __shfl_xor(part[0], 32, kWave);
         if ((lane & 32) == 0 && (lane & (64 / RPW - 1)) == 0)
-            store_h<WT>(a.out, int64_t(p) * a.I + col0 + qi, silu(part[0]) * up);
+            store_act<WT>(a.out, int64_t(p) * a.I + col0 + qi, silu(part[0]) * up);
     }
 }
 
@@ -172,7 +172,7 @@ __global__ void __launch_bounds__(64 * kDownWaves) k_decode_down(const DecodeArg
         const int qi = dev::group_reduce_split<NPASS, LPR>(part, lane);
         const int r = row0 + qi * RPP + g;
         if ((lr & (LPR / NPASS - 1)) == 0 && r < a.nrows)
-            reinterpret_cast<float*>(a.out)[int64_t(p) * a.H + r] = part[0];
+            store_act<WT>(a.out, int64_t(p) * a.H + r, part[0]);
         first = false;
         have = it.next(p, t);
     }
@@ -230,7 +230,7 @@ bool decode_shape_supported(const moe_config& c) {
 }
 
 hipError_t launch_ffn_decode(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
-                             const void* slot_base, const void* shared, const DecodeList& list, float* o, void* ws,
+                             const void* slot_base, const void* shared, const DecodeList& list, void* o, void* ws,
                              hipStream_t s) {
     const int gu_ch = ffn::chunks_per_row(c.w_dtype, c.hidden), d_ch = ffn::chunks_per_row(c.w_dtype, c.inter);
     int lpr, cpld;
@@ -262,7 +262,7 @@ hipError_t launch_ffn_decode(const moe_config& c, const BlobLayout& lay, const v
     a.off_w = lay.d;
     a.off_s = lay.d_scale;
     a.act = hbuf;
-    a.out = reinterpret_cast<uint8_t*>(o);
+    a.out = static_cast<uint8_t*>(o);
     a.K = c.inter;
     a.nrows = c.hidden;
     switch (c.w_dtype) {

@@ -356,7 +356,7 @@ __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
             }
         }
     } else {
-        float* o = static_cast<float*>(a.out);
+        uint16_t* o = static_cast<uint16_t*>(a.out);       // pair outputs, bf16
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -365,7 +365,8 @@ __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
                 if (row < rows) {
                     const int64_t p = shared ? int64_t(a.T) * a.k + row : a.perm[base + row];
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) o[p * a.H + n0 + wn * TN + j * MF + lane % MF] = acc[i][j][q];
+                    for (int j = 0; j < FN; ++j)
+                        o[p * a.H + n0 + wn * TN + j * MF + lane % MF] = dev::f32_to_bf16_bits(acc[i][j][q]);
                 }
             }
     }
@@ -603,8 +604,8 @@ __global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
         int32_t* dst = reinterpret_cast<int32_t*>(lds8 + dma::PR * dma::OSTR);
         for (int r = tid_; r < dma::BM; r += dma::kThreads)
             dst[r] = m0 + r >= rows ? -1 : shared ? a.T * a.k + m0 + r : a.perm[base + m0 + r];
-        float* o = static_cast<float*>(a.out);
-        constexpr int CH = dma::BN / 4;                      // 16-byte chunks per fp32 row of the tile
+        uint16_t* o = static_cast<uint16_t*>(a.out);        // pair outputs, bf16
+        constexpr int CH = dma::BN / 8;                      // 8-value chunks (16 bytes of bf16) per row
         for (int pass = 0; pass < dma::BM / dma::PR; ++pass) {
             if (active) {
 #pragma unroll
@@ -625,9 +626,16 @@ __global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
             for (int idx = tid_; idx < dma::PR * CH; idx += dma::kThreads) {
                 const int r = idx / CH, c = idx % CH;
                 const int d = dst[pass * dma::PR + r];
-                if (d >= 0)
-                    *reinterpret_cast<dev::u32x4*>(o + int64_t(d) * a.H + n0 + c * 4) =
-                        *reinterpret_cast<const dev::u32x4*>(ot + r * dma::OSTR + c * 16);
+                if (d >= 0) {
+                    const float4 u = *reinterpret_cast<const float4*>(ot + r * dma::OSTR + c * 32);
+                    const float4 v = *reinterpret_cast<const float4*>(ot + r * dma::OSTR + c * 32 + 16);
+                    dev::u32x4 pk;
+                    pk[0] = dev::pack_bf16x2(u.x, u.y);
+                    pk[1] = dev::pack_bf16x2(u.z, u.w);
+                    pk[2] = dev::pack_bf16x2(v.x, v.y);
+                    pk[3] = dev::pack_bf16x2(v.z, v.w);
+                    *reinterpret_cast<dev::u32x4*>(o + int64_t(d) * a.H + n0 + c * 8) = pk;
+                }
             }
             __syncthreads();
         }
@@ -672,7 +680,7 @@ bool gemm_shape_supported(const moe_config& c) {
 
 hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
                            const int32_t* offsets, const int32_t* perm, const void* slot_base,
-                           const void* shared, const ExpertList& list, float* o, void* ws, hipStream_t s) {
+                           const void* shared, const ExpertList& list, void* o, void* ws, hipStream_t s) {
     const WsLayout W = ws_layout(c, T);
     int32_t* tiles = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + W.tiles);
     const bool fp4 = c.w_dtype == MOE_W_MXFP4;

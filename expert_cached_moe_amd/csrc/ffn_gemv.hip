@@ -126,7 +126,7 @@ k_gemv(const GemvArgs a) {
                 if (GU) {
                     s_sum[bi][row - blockIdx.x * RPB] = part[0];
                 } else if (row < a.nrows) {
-                    reinterpret_cast<float*>(a.out)[int64_t(p) * a.H + row] = part[0];
+                    store_act<WT>(a.out, int64_t(p) * a.H + row, part[0]);
                 }
             }
         }
@@ -139,10 +139,7 @@ k_gemv(const GemvArgs a) {
                 const int p = shared ? a.T * a.k + i : a.perm[base + i];
                 const float hv = silu(s_sum[bi][r]) * s_sum[bi][r + 16];
                 const int64_t col = int64_t(blockIdx.x) * 16 + r;
-                if (WT == WT_F32)
-                    reinterpret_cast<float*>(a.out)[int64_t(p) * a.I + col] = hv;
-                else
-                    reinterpret_cast<uint16_t*>(a.out)[int64_t(p) * a.I + col] = dev::f32_to_bf16_bits(hv);
+                store_act<WT>(a.out, int64_t(p) * a.I + col, hv);
             }
             __syncthreads();
         }
@@ -207,7 +204,7 @@ bool gemv_shape_supported(const moe_config& c) {
 
 hipError_t launch_ffn_gemv(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
                            const int32_t* offsets, const int32_t* perm, const void* slot_base,
-                           const void* shared, const ExpertList& list, float* o, void* ws, hipStream_t s) {
+                           const void* shared, const ExpertList& list, void* o, void* ws, hipStream_t s) {
     Variant vgu, vd;
     if (!pick(chunks_per_row(c.w_dtype, c.hidden), &vgu) || !pick(chunks_per_row(c.w_dtype, c.inter), &vd))
         return hipErrorInvalidValue;
@@ -237,7 +234,7 @@ hipError_t launch_ffn_gemv(const moe_config& c, const BlobLayout& lay, const voi
     a.off_w = lay.d;
     a.off_s = lay.d_scale;
     a.act = hbuf;
-    a.out = reinterpret_cast<uint8_t*>(o);
+    a.out = static_cast<uint8_t*>(o);
     a.K = c.inter;
     a.nrows = c.hidden;
     return launch_wt<false>(c.w_dtype, a, vd, list.n, s);

@@ -117,7 +117,7 @@ struct DecodeList {
 };
 
 hipError_t launch_ffn_decode(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
-                             const void* slot_base, const void* shared, const DecodeList& list, float* o, void* ws,
+                             const void* slot_base, const void* shared, const DecodeList& list, void* o, void* ws,
                              hipStream_t s);
 bool decode_shape_supported(const moe_config& c);
 
@@ -128,20 +128,20 @@ hipError_t launch_route(const moe_config& c, const float* logits, int32_t T, int
 // Returns hipSuccess, or hipErrorInvalidValue when no kernel variant fits the shape.
 hipError_t launch_ffn_gemv(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
                            const int32_t* offsets, const int32_t* perm, const void* slot_base,
-                           const void* shared, const ExpertList& list, float* o, void* ws,
+                           const void* shared, const ExpertList& list, void* o, void* ws,
                            hipStream_t s);
 bool gemv_shape_supported(const moe_config& c);
 
 
 hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
                            const int32_t* offsets, const int32_t* perm, const void* slot_base,
-                           const void* shared, const ExpertList& list, float* o, void* ws,
+                           const void* shared, const ExpertList& list, void* o, void* ws,
                            hipStream_t s);
 bool gemm_shape_supported(const moe_config& c);
 
 hipError_t launch_router_logits(const moe_config& c, const void* x, int32_t T, const float* wr, float* out,
                                 hipStream_t s);
-hipError_t launch_merge(const moe_config& c, const float* o, const int32_t* ids, const float* w,
+hipError_t launch_merge(const moe_config& c, const void* o, const int32_t* ids, const float* w,
                         const uint32_t* gpu_mask, int32_t with_shared, const float* y_host,
                         int32_t T, void* out, hipStream_t s);
 

@@ -22,7 +22,7 @@ extern "C" {
 
 int moe_prefill_stream(moe_ctx* ctx, void* d_layer_bufs, int32_t n_buffers, const float* d_logits, const void* d_x,
                        int32_t T, const void* d_shared, int32_t* d_topk_ids, float* d_topk_w, int32_t* d_counts,
-                       int32_t* d_offsets, int32_t* d_perm, int32_t* d_inv, float* d_o, void* d_ws, void* d_out,
+                       int32_t* d_offsets, int32_t* d_perm, int32_t* d_inv, void* d_o, void* d_ws, void* d_out,
                        hipStream_t s, hipStream_t side) {
     if (!ctx) return MOE_EINVAL;
     const moe_config& c = ctx->cfg;

@@ -28,7 +28,9 @@ class LayerBuffers:
         self.offsets = torch.empty(self.E + 1, dtype=torch.int32, device=dev)
         self.perm = torch.empty(n, dtype=torch.int32, device=dev)
         self.inv = torch.empty(n, dtype=torch.int32, device=dev)
-        self.o = torch.empty(max(1, B.moe_pair_rows(cfg, max_T)) * self.H, dtype=torch.float32, device=dev)
+        # pair outputs in the activation dtype: fp32 for fp32 weights, bf16 bits (int16 storage) otherwise
+        o_dtype = torch.float32 if cfg.w_dtype == B.MOE_W_F32 else torch.int16
+        self.o = torch.empty(max(1, B.moe_pair_rows(cfg, max_T)) * self.H, dtype=o_dtype, device=dev)
 
     def close(self):
         if self.ctx:

@@ -144,7 +144,8 @@ int64_t moe_expert_bytes(const moe_config* cfg);
  * its first kilobytes (queue counters of the decode FFN) zeroed again, the rest is
  * scratch.  Calls that share a workspace must be ordered (one stream, or events). */
 int64_t moe_workspace_bytes(const moe_config* cfg, int32_t max_T);
-/* Rows of the pair-output buffer d_o for T tokens: T*k (+ T with a shared expert). */
+/* Rows of the pair-output buffer d_o for T tokens: T*k (+ T with a shared expert).  Each
+ * row holds H values in the activation dtype (fp32 for fp32 weights, else bf16). */
 int64_t moe_pair_rows(const moe_config* cfg, int32_t T);
 
 /* Pack one expert from natural layout into a blob (host memory, moe_expert_bytes).
@@ -236,8 +237,9 @@ int moe_upload(moe_ctx* ctx, void* d_dst, const void* h_src, int64_t bytes, hipS
  *   d_slot_base + h_slots[i]*moe_expert_bytes; with with_shared = 1 also
  *   o[T*k + t] for the shared expert blob d_shared (all tokens).
  *   d_x [T][H] activations; h_experts / h_slots: host arrays of n (<= E) distinct
- *   expert ids and slot indices; d_o [moe_pair_rows][H] fp32 (rows of unlisted
- *   experts are not written); d_ws: moe_workspace_bytes(max_T >= T).
+ *   expert ids and slot indices; d_o [moe_pair_rows][H] in the activation dtype,
+ *   each pair's result rounded once (rows of unlisted experts are not written);
+ *   d_ws: moe_workspace_bytes(max_T >= T).
  *   Which tokens use an expert comes from h_topk_ids (host copy [T][k] of the
  *   step's ids, as moe_lru_step consumes) when given and T <= 8; the kernels then
  *   do not read d_offsets / d_perm and need not wait for moe_route.  Otherwise
@@ -247,7 +249,7 @@ int moe_upload(moe_ctx* ctx, void* d_dst, const void* h_src, int64_t bytes, hipS
 int moe_expert_ffn(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* h_topk_ids,
                    const int32_t* d_offsets, const int32_t* d_perm, const void* d_slot_base,
                    const int32_t* h_experts, const int32_t* h_slots, int32_t n, const void* d_shared,
-                   int32_t with_shared, float* d_o, void* d_ws, hipStream_t s);
+                   int32_t with_shared, void* d_o, void* d_ws, hipStream_t s);
 
 /* CPU SwiGLU experts of the plan's host set from the bound host pool:
  * h_y[t] = sum over j with topk_ids[t][j] in plan->host of w[t][j]*FFN(x_t),
@@ -261,9 +263,10 @@ int moe_host_ffn(moe_ctx* ctx, const void* h_x, int32_t T, const int32_t* h_topk
 /* Gate-weighted un-permute and exact merge of the partial sums (async on s):
  *   out[t] = cast( sum_{j=0..k-1, topk_ids[t][j] in h_gpu_experts} w[t][j]*o[t*k+j]
  *                  + (with_shared ? o[T*k+t] : 0) + (d_y_host ? y_host[t] : 0) )
- * in fp32, in that order; out is fp32 (fp32 weights) or bf16 [T][H].
+ * in fp32, in that order; d_o as written by moe_expert_ffn (activation dtype);
+ * out is fp32 (fp32 weights) or bf16 [T][H].
  * ([B] "The q* Policy": the partial sums merge exactly after the layer.) */
-int moe_merge_partial(moe_ctx* ctx, const float* d_o, const int32_t* d_topk_ids, const float* d_topk_w,
+int moe_merge_partial(moe_ctx* ctx, const void* d_o, const int32_t* d_topk_ids, const float* d_topk_w,
                       const int32_t* h_gpu_experts, int32_t n_gpu, int32_t with_shared,
                       const float* d_y_host, int32_t T, void* d_out, hipStream_t s);
 
@@ -292,7 +295,7 @@ int moe_merge_partial(moe_ctx* ctx, const float* d_o, const int32_t* d_topk_ids,
  * leave part of the chunk enqueued. */
 int moe_prefill_stream(moe_ctx* ctx, void* d_layer_bufs, int32_t n_buffers, const float* d_logits,
                        const void* d_x, int32_t T, const void* d_shared, int32_t* d_topk_ids, float* d_topk_w,
-                       int32_t* d_counts, int32_t* d_offsets, int32_t* d_perm, int32_t* d_inv, float* d_o,
+                       int32_t* d_counts, int32_t* d_offsets, int32_t* d_perm, int32_t* d_inv, void* d_o,
                        void* d_ws, void* d_out, hipStream_t s, hipStream_t side);
 
 #ifdef __cplusplus

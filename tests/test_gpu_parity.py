@@ -154,8 +154,9 @@ def _decode_case(B, name, T, frac, seed, host_ids=True):
     err = rel_err_rows(y, ref)
     tol = TOL[wl.wdtype]
     assert err.max() <= tol, (name, T, err.max())
-    # per-pair expert outputs (fp32, before the bf16 cast): tighter bound
-    o = G.L.o[: (T * wl.k + (T if ws else 0)) * wl.H].cpu().numpy().reshape(-1, wl.H)
+    # per-pair expert outputs (activation dtype, before the gate-weighted sum): tighter bound
+    rows = T * wl.k + (T if ws else 0)
+    o = out_f64(G.L.o[: rows * wl.H], wl, rows)
     for t in range(T):
         for j in range(wl.k):
             e = int(ids[t, j])
@@ -247,5 +248,7 @@ def test_prefill_full_size_sampled(B, name, n_sample):
     ref = oracle.moe_layer(xs, rids[sample], g32[sample], conv, shared=conv(wl.E) if ws else None)
     err = rel_err_rows(y[sample], ref)
     assert err.max() <= TOL[wl.wdtype], err.max()
-    assert np.median(err) <= 4e-3, np.median(err)       # typical error of bf16 h rounding, well under the bound
+    # typical error of two bf16 roundings (h, then each pair output, up to 2^-9 relative
+    # each), well under the bound
+    assert np.median(err) <= 6e-3, np.median(err)
     G.L.close()
