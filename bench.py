@@ -85,8 +85,8 @@ def payload_bytes(wl):
 # sources hash to the value it was taken with.
 DECODE_SOURCES = ("ffn_decode.hip", "ffn_common.h", "device_common.h")
 TRAFFIC = {
-    ("a3b_decode_bf16", 1): {"sha256": "768e8f298aac8d4f21991791b1ad6019b2b622445673198f55c263eb3fb0d613",
-                             "fetch_kib": 24608.8 + 12354.0, "write_kib": 48.0 + 64.0},
+    ("a3b_decode_bf16", 1): {"sha256": "0e9a83a2c709e29e51b80f2ba14e6ee4ed0415381f3daac5c0417152dc76c084",
+                             "fetch_kib": 24608.8 + 12360.5, "write_kib": 48.0 + 32.0},
 }
 FETCH_FACTOR = 262144.0 / 131080.0
 WRITE_FACTOR = 1.0
