@@ -132,8 +132,8 @@ class GpuLayer:
         return out
 
 
-def _decode_case(B, name, T, frac, seed, host_ids=True):
-    wl = synth.workload(name)
+def _decode_case(B, name, T, frac, seed, host_ids=True, wl=None):
+    wl = wl or synth.workload(name)
     lg, _ = synth.zipf_reuse_trace(wl, T, 3, tag=seed)
     logits = lg[2]
     ids, gates = oracle.route(logits, wl.k)
@@ -179,6 +179,18 @@ def _decode_case(B, name, T, frac, seed, host_ids=True):
 def test_decode_ffn_merge_parity(B, name, T, frac):
     print(f"[decode] {name} T={T} frac={frac}", flush=True)
     _decode_case(B, name, T, frac, seed=T * 10 + int(frac * 2))
+
+
+@pytest.mark.parametrize("wdtype,H,I,T", [("f32", 512, 256, 1), ("f32", 512, 256, 5), ("bf16", 1024, 512, 1),
+                                          ("bf16", 1024, 512, 8)])
+def test_decode_other_shapes(B, wdtype, H, I, T):
+    """Decode at hidden/intermediate sizes other than the workloads' (16 experts, top-4):
+    the kernels pick their lanes-per-row and chunks-per-lane from the shape."""
+    print(f"[decode-other-shapes] {wdtype} H={H} I={I} T={T}", flush=True)
+    import dataclasses
+    base = synth.workload("tiny_fp32" if wdtype == "f32" else "a3b_decode_bf16")
+    wl = dataclasses.replace(base, name=f"{wdtype}_{H}x{I}", H=H, I=I, E=16, k=4, C=16, batches=(T,))
+    _decode_case(B, None, T, 0.75, seed=T + 300, wl=wl)
 
 
 @pytest.mark.parametrize("name,T", [("tiny_fp32", 3), ("a3b_decode_bf16", 8), ("v4flash_mxfp4", 2)])
