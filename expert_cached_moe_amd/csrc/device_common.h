@@ -27,8 +27,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return uint16_t(u >> 16);
 }
 
+// Two fp32 values to packed bf16 (lo in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return uint32_t(f32_to_bf16_bits(lo)) | (uint32_t(f32_to_bf16_bits(hi)) << 16);
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // Sum of NV values held by every lane of a group of G consecutive lanes (G a power of

@@ -91,6 +91,11 @@ __device__ __forceinline__ float chunk_dot<WT_FP4>(const uint4& w, const ActChun
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu from the hardware exp2 and reciprocal (about 1 ulp each), for values that are
+// rounded to bf16 (8 significant bits) right after.
+__device__ __forceinline__ float silu_fast(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
 
 
 // 16-byte weight chunk `ch` of a row, streamed (non-temporal: read once per step).

@@ -20,6 +20,8 @@
 // from that XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "ffn_common.h"
 #include "internal.h"
@@ -138,8 +140,22 @@ struct GemmArgs {
     int32_t T, k, K, N;        // K: reduction length, N: output columns of the matrix
     int32_t I, H;
     int32_t grid;              // launched workgroups (a multiple of the XCD count)
+    int32_t mode;              // 0: GEMM 1 (A rows gathered from x), 1: GEMM 2 (A = h)
     ExpertList list;
 };
+
+// Logical tile of workgroup b, or -1.  The real tile count (the list's row tiles times
+// the column tiles) is cut into kXcds contiguous ranges, one per XCD (workgroups are dealt
+// round-robin to the XCDs), so each XCD's L2 holds the A rows and weights of a few
+// experts at a time and every XCD gets an equal share.  The grid is sized for the most
+// row tiles a list can have; the workgroups past an XCD's share exit at once.
+__device__ __forceinline__ int xcd_tile(int b, int n_slots, int n_tiles) {
+    const int total = n_slots * n_tiles;
+    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const int i = b / kXcds;
+    const int lid = (b % kXcds) * per_xcd + i;
+    return i < per_xcd && lid < total ? lid : -1;
+}
 
 // MXFP4 -> bf16 of 32 elements (16 code bytes) with the block scale folded in.
 __device__ __forceinline__ void fp4_to_bf16(const uint4 codes, uint8_t s, uint4 out[4]) {
@@ -155,6 +171,9 @@ __device__ __forceinline__ void fp4_to_bf16(const uint4 codes, uint8_t s, uint4 
                             __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
     }
 }
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint16_t bf16_bits(float v) { return uint16_t(dev::pack_bf16x2(v, 0.0f)); }
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -174,13 +193,10 @@ __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave / WN, wn = wave % WN;
 
-    // XCD-contiguous logical tile id (workgroups are dealt round-robin to the XCDs)
-    const int b = blockIdx.x;
-    const int per_xcd = a.grid / kXcds;
-    const int lid = (b % kXcds) * per_xcd + b / kXcds;
     const int n_tiles = a.N / BN;
+    const int lid = xcd_tile(blockIdx.x, a.tiles[0], n_tiles);
+    if (lid < 0) return;
     const int slot = lid / n_tiles, nt = lid % n_tiles;
-    if (slot >= a.tiles[0]) return;
     const int tinfo = a.tiles[1 + slot];
     const int ei = tinfo >> 16, mt = tinfo & 0xFFFF;
     const int entry = a.list.ent[ei];
@@ -333,7 +349,7 @@ __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
                         const int row = row_of(i, q);
                         if (row < rows) {
                             const int64_t hrow = shared ? int64_t(a.T) * a.k + row : base + row;
-                            h[hrow * a.I + col] = dev::f32_to_bf16_bits(ffn::silu(acc[i][2 * jj][q]) * acc[i][2 * jj + 1][q]);
+                            h[hrow * a.I + col] = dev::f32_to_bf16_bits(ffn::silu_fast(acc[i][2 * jj][q]) * acc[i][2 * jj + 1][q]);
                         }
                     }
             }
@@ -350,7 +366,7 @@ __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
                         const int row = row_of(i, q);
                         if (gate_lane && row < rows) {
                             const int64_t hrow = shared ? int64_t(a.T) * a.k + row : base + row;
-                            h[hrow * a.I + col] = dev::f32_to_bf16_bits(ffn::silu(acc[i][j][q]) * up);
+                            h[hrow * a.I + col] = dev::f32_to_bf16_bits(ffn::silu_fast(acc[i][j][q]) * up);
                         }
                     }
             }
@@ -456,12 +472,10 @@ __global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave / dma::WN, wn = wave % dma::WN;
-    const int b = blockIdx.x;
-    const int per_xcd = a.grid / kXcds;
-    const int lid = (b % kXcds) * per_xcd + b / kXcds;
     const int n_tiles = a.N / dma::BN;
+    const int lid = xcd_tile(blockIdx.x, a.tiles[0], n_tiles);
+    if (lid < 0) return;
     const int slot = lid / n_tiles;
-    if (slot >= a.tiles[0]) return;
     const int tinfo = a.tiles[1 + slot];
     const int ei = tinfo >> 16;
     int mt = tinfo & 0xFFFF, nt = lid % n_tiles;
@@ -584,7 +598,7 @@ __global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
                         const int q = (lane % 32) < 16 ? q1 : q1 + 4;
                         const int r = wm * dma::TM + i * 32 + 8 * (q / 4) + (lane / 32) * 4 + (q % 4);
                         *reinterpret_cast<uint16_t*>(ht + r * dma::HSTR + col * 2) =
-                            dev::f32_to_bf16_bits(ffn::silu(g) * u);
+                            dev::f32_to_bf16_bits(ffn::silu_fast(g) * u);
                     }
                 }
         }
@@ -642,6 +656,335 @@ __global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- large-tile bf16 GEMM
+// 256 x 256 output tiles, 4 waves (2 x 2) of 128 x 128 = 4 x 4 fragments of 32x32x16
+// MFMA.  Per K = 16 a wave reads 8 fragments (8 KiB) from LDS for 16 MFMAs: half the
+// LDS bytes per flop of 64 x 64 wave tiles.  K slices of BK = 64 (128-byte rows, so every
+// row segment a load touches is a whole cache line) are filled by direct global->LDS
+// loads into two 64 KiB stage buffers; with the 256 accumulators in registers this is
+// one workgroup per CU.  The workgroups are persistent: each walks its XCD's share of the
+// tiles, and the first K slice of its next tile is loaded while the current tile's last
+// slice and epilogue run (the epilogue is staged in the LDS above the first buffer), so
+// the per-tile start-up and the output stores overlap the MFMAs.  Waves whose rows lie
+// partly past the expert's last row run only the fragments that hold rows (FA of FM).
+#ifndef MOE_GEMM_BIG
+#define MOE_GEMM_BIG 1
+#endif
+namespace big {
+constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 2, MF = 32;
+constexpr int NW = WM * WN, kThreads = NW * kWave;
+constexpr int TM = BM / WM, TN = BN / WN, FM = TM / MF, FN = TN / MF;
+constexpr int ROWB = BK * 2, CPR = ROWB / 16;       // 128-byte LDS rows of 8 chunks
+constexpr int STAGE_BYTES = (BM + BN) * ROWB;       // 64 KiB
+constexpr int Q = STAGE_BYTES / 1024 / NW;          // 1 KiB load instructions per wave per slice
+constexpr int QA = BM * ROWB / 1024 / NW;           // the first QA of them load A rows
+constexpr int EPI = STAGE_BYTES;                    // h staging (GEMM 1) starts above buffer 0
+constexpr int HSTR = BN + 16;                       // h staging row: BN/2 bf16 + 16 bytes
+constexpr int ROWTAB = EPI + BM * HSTR;             // output row of each tile row (GEMM 2)
+constexpr int kLdsBytes = ROWTAB + BM * 4;
+static_assert(kLdsBytes <= 160 * 1024 && ROWTAB >= 2 * STAGE_BYTES, "LDS per CU; the row table is outside the stages");
+static_assert(Q * NW * 1024 == STAGE_BYTES && QA * NW * 1024 == BM * ROWB, "stage split");
+static_assert(FM * MF == TM && FN * MF == TN && FM == 4, "wave tile (the FA dispatch covers 0..4)");
+static_assert(kThreads == BM, "one output row per thread in the epilogue bookkeeping");
+// chunk c of row r sits at slot c ^ ((r >> 1) & 7): two 128-byte rows share a 256-byte
+// bank window, and the 32 rows of a fragment read land on distinct banks
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// One tile as this thread sees it.
+struct Tile {
+    int m0, n0, rows, fa;
+    int obase;                  // output row of tile row 0 when the rows are consecutive (h; shared expert)
+    int orow;                   // output row of this thread's tile row (epilogue), -1 past the end
+    const uint8_t* bbase;       // weight row n0 at K offset 0 (wave-uniform)
+    uint32_t ao[QA];            // byte offsets (from a_src) of the A rows of this lane's QA load chunks
+};
+
+// Byte offset of this lane's chunk within a weight-row block: load QA + q reads weight row
+// (wave + NW (QA + q)) * 64 + lane) / 8 - BM = rb + 32 q; the chunk (source-side swizzle: the
+// LDS side of a load is linear) is the same for every q, and for the A loads too.
+__device__ __forceinline__ int lane_chunk() {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    return swz((wave * 64 + lane) / CPR, lane % CPR);
+}
+
+__device__ __forceinline__ Tile make_tile(const GemmArgs& a, int lid, int n_tiles) {
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int wm = wave / WN;
+    Tile t;
+    const int slot = lid / n_tiles, nt = lid % n_tiles;
+    const int tinfo = a.tiles[1 + slot];
+    const int ei = tinfo >> 16, mt = tinfo & 0xFFFF;
+    const int entry = a.list.ent[ei];
+    const int e = entry & 1023;
+    const bool shared = e == kSharedTag;
+    const uint8_t* blob = shared ? a.shared_blob : a.slot_base + int64_t(entry >> 10) * a.blob_bytes;
+    const int base = shared ? 0 : a.offsets[e];
+    t.rows = shared ? a.T : a.offsets[e + 1] - base;
+    t.m0 = mt * BM;
+    t.n0 = nt * BN;
+    const int fa = (t.rows - t.m0 - wm * TM + 31) / 32;   // fragment rows of this wave that hold rows
+    t.fa = __builtin_amdgcn_readfirstlane(fa < 0 ? 0 : fa > FM ? FM : fa);
+    const uint32_t arow_bytes = uint32_t(a.K) * 2;
+    const uint32_t c16 = uint32_t(lane_chunk()) * 16;
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+        const int r = ((wave + NW * q) * 64 + lane) / CPR;
+        const int rr = t.m0 + r < t.rows ? t.m0 + r : 0;        // rows past the end load row 0 (dropped)
+        uint32_t srow;
+        if (a.mode == 0)
+            srow = shared ? rr : a.perm[base + rr] / a.k;
+        else
+            srow = shared ? a.T * a.k + rr : base + rr;
+        t.ao[q] = srow * arow_bytes + c16;
+    }
+    t.bbase = blob + a.off_w + int64_t(t.n0) * arow_bytes;
+    t.obase = (shared ? a.T * a.k : base) + t.m0;
+    const int r = tid;                                           // epilogue: tile row tid
+    t.orow = t.m0 + r >= t.rows ? -1 : a.mode == 0 || shared ? t.obase + r : a.perm[base + t.m0 + r];
+    return t;
+}
+
+// Loads of one K slice into stage buffer buf: A rows at a_src + ao[q] + koff, weight rows
+// at bbase + boff + koff (boff: this lane's offset in the tile's weight rows).
+__device__ __forceinline__ void issue(uint8_t* lds8, const uint8_t* a_src, const uint32_t (&ao)[QA],
+                                      const uint8_t* bbase, uint32_t boff, uint32_t bstride, uint32_t koff, int buf) {
+    const int wave = threadIdx.x / kWave;
+    uint8_t* st = lds8 + buf * STAGE_BYTES;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const uint8_t* src = q < QA ? a_src + (ao[q] + koff) : bbase + (boff + (q - QA) * bstride + koff);
+        __builtin_amdgcn_global_load_lds(src, st + (wave + NW * q) * 1024, 16, 0, 0);
+    }
+}
+}  // namespace big
+
+// Barrier that hands direct-to-LDS data to the other waves: every wave first waits for its
+// own loads (they write blocks the other waves read; a plain __syncthreads() only waits for
+// what this wave's own later code reads, so it may leave them in flight).
+__device__ __forceinline__ void barrier_loads() {
+    __builtin_amdgcn_s_waitcnt(0);      // vmcnt(0) expcnt(0) lgkmcnt(0)
+    __syncthreads();
+}
+
+// One tile for a wave that computes FA fragment rows (0..FM).  On entry the tile's slice 0
+// is in flight into buffer 0; before the last slice the next tile's slice 0 is issued into
+// buffer 0 (for the last tile of the workgroup, a harmless reload of this tile's last slice).
+template <int MODE, int FA>
+__device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const big::Tile& t, const big::Tile& nx,
+                                         bool has_next) {
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int wm = wave / big::WN, wn = wave % big::WN;
+    const int nk = a.K / big::BK;
+    const uint32_t bstride = uint32_t(a.K) * 2 * (big::NW * 64 / big::CPR);   // 32 weight rows
+    const uint32_t boff = uint32_t(((wave + big::NW * big::QA) * 64 + lane) / big::CPR - big::BM) * uint32_t(a.K) * 2 +
+                          uint32_t(big::lane_chunk()) * 16;
+    constexpr int NA = FA > 0 ? FA : 1;
+    f32x16 acc[NA][big::FN];
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+        for (int j = 0; j < big::FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    // fragments of K sub-step kk (16 wide) of a stage; two register sets, so the reads
+    // of sub-step kk + 1 are in flight while the MFMAs of kk run
+    auto frag = [&](const uint8_t* as_, int kk, bf16x8 (&fa)[NA], bf16x8 (&fb)[big::FN]) {
+        const uint8_t* bs_ = as_ + big::BM * big::ROWB;
+        const int c = kk * 2 + lane / 32;
+#pragma unroll
+        for (int i = 0; i < FA; ++i) {
+            const int R = wm * big::TM + i * 32 + lane % 32;
+            fa[i] = *reinterpret_cast<const bf16x8*>(as_ + R * big::ROWB + (big::swz(R, c) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < big::FN; ++j) {
+            const int R = wn * big::TN + j * 32 + lane % 32;
+            fb[j] = *reinterpret_cast<const bf16x8*>(bs_ + R * big::ROWB + (big::swz(R, c) << 4));
+        }
+    };
+    auto mma = [&](const bf16x8 (&fa)[NA], const bf16x8 (&fb)[big::FN]) {
+#pragma unroll
+        for (int i = 0; i < FA; ++i)
+#pragma unroll
+            for (int j = 0; j < big::FN; ++j) acc[i][j] = mfma(fa[i], fb[j], acc[i][j]);
+    };
+    // schedule of one sub-step: its MFMAs with the next sub-step's LDS reads placed one
+    // after each of the first MFMAs
+    constexpr int NR = FA + big::FN, NM = FA * big::FN;
+    auto sched = [&]() {
+        if constexpr (NM >= NR) {
+#pragma unroll
+            for (int n = 0; n < NR; ++n) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if constexpr (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+        }
+    };
+
+    // Slice ks is read from buffer ks & 1 (nk is even).  The barrier of slice ks sits
+    // before its last sub-step: by then every wave has read all of slice ks (so its buffer
+    // can take slice ks + 2) and the loads of slice ks + 1, issued one slice earlier, have
+    // landed (so the last sub-step's MFMAs overlap the reads of the next slice's first
+    // sub-step).  The loop body is straight-line and the last slice is peeled, which keeps
+    // the accumulators in place across iterations.
+    bf16x8 fa0[NA], fb0[big::FN], fa1[NA], fb1[big::FN];
+    barrier_loads();            // slice 0 has landed; the previous tile's epilogue is done with the LDS
+    big::issue(lds8, a.a_src, t.ao, t.bbase, boff, bstride, big::ROWB, 1);
+    if (MODE == 1) reinterpret_cast<int32_t*>(lds8 + big::ROWTAB)[tid] = t.orow;   // read after later barriers
+    if constexpr (FA > 0) frag(lds8, 0, fa0, fb0);
+    for (int ks = 0; ks + 1 < nk; ++ks) {
+        const uint8_t* as_ = lds8 + (ks & 1) * big::STAGE_BYTES;
+        if constexpr (FA > 0) {
+            frag(as_, 1, fa1, fb1);
+            mma(fa0, fb0);
+            frag(as_, 2, fa0, fb0);
+            mma(fa1, fb1);
+            frag(as_, 3, fa1, fb1);
+            mma(fa0, fb0);
+            sched();
+            sched();
+            sched();
+        }
+        barrier_loads();
+        {
+            // slice ks + 2 into the buffer slice ks leaves; past the end, the next tile's slice 0
+            // (or, after the last tile, this tile's last slice again: never read)
+            const bool nxt = ks + 2 >= nk;
+            const bool other = nxt && has_next;
+            const uint32_t koff = uint32_t(nxt ? (has_next ? 0 : nk - 1) : ks + 2) * big::ROWB;
+            uint32_t ao[big::QA];
+#pragma unroll
+            for (int q = 0; q < big::QA; ++q) ao[q] = other ? nx.ao[q] : t.ao[q];
+            big::issue(lds8, a.a_src, ao, other ? nx.bbase : t.bbase, boff, bstride, koff, ks & 1);
+        }
+        if constexpr (FA > 0) {
+            frag(lds8 + ((ks + 1) & 1) * big::STAGE_BYTES, 0, fa0, fb0);
+            mma(fa1, fb1);
+            sched();
+        }
+    }
+    if constexpr (FA > 0) {
+        const uint8_t* as_ = lds8 + big::STAGE_BYTES;       // slice nk - 1 (odd)
+        frag(as_, 1, fa1, fb1);
+        mma(fa0, fb0);
+        frag(as_, 2, fa0, fb0);
+        mma(fa1, fb1);
+        frag(as_, 3, fa1, fb1);
+        mma(fa0, fb0);
+        mma(fa1, fb1);
+    }
+
+    // Epilogue through the LDS above buffer 0 (buffer 0 is taking the next tile's first
+    // slice): the tile is staged there and written out as whole rows, 16 bytes a lane.
+    uint8_t* stg = lds8 + big::EPI;
+    __syncthreads();            // every wave is done with slice nk - 1 (buffer 1)
+    if (MODE == 0) {
+        // SwiGLU: in a 32-wide fragment lanes 0-15 hold gate and lanes 16-31 up for the
+        // same 16 h columns; permlane16_swap of elements q1 and q1+4 hands every lane a
+        // (gate, up) pair: lanes 0-15 of each half those of q1, lanes 16-31 those of q1+4.
+#pragma unroll
+        for (int i = 0; i < FA; ++i)
+#pragma unroll
+            for (int j = 0; j < big::FN; ++j) {
+                const int col = (wn * big::TN + j * 32) / 2 + lane % 16;
+                float hv[8];
+#pragma unroll
+                for (int qq = 0; qq < 8; ++qq) {
+                    const int q1 = (qq / 4) * 8 + qq % 4;
+                    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i][j][q1]),
+                                                                     __float_as_uint(acc[i][j][q1 + 4]), false, false);
+                    hv[qq] = ffn::silu_fast(__uint_as_float(sw[0])) * __uint_as_float(sw[1]);
+                }
+#pragma unroll
+                for (int qq = 0; qq < 8; ++qq) {
+                    const int q1 = (qq / 4) * 8 + qq % 4;
+                    const int q = (lane % 32) < 16 ? q1 : q1 + 4;
+                    const int r = wm * big::TM + i * 32 + 8 * (q / 4) + (lane / 32) * 4 + (q % 4);
+                    *reinterpret_cast<uint16_t*>(stg + r * big::HSTR + col * 2) = bf16_bits(hv[qq]);
+                }
+            }
+        __syncthreads();
+        constexpr int CH = big::BN / 16;                     // 16-byte chunks per h row of the tile
+        uint16_t* h = static_cast<uint16_t*>(a.out);
+#pragma unroll 4
+        for (int idx = tid; idx < big::BM * CH; idx += big::kThreads) {
+            const int r = idx / CH, c = idx % CH;
+            if (t.m0 + r < t.rows)
+                *reinterpret_cast<dev::u32x4*>(h + int64_t(t.obase + r) * a.I + t.n0 / 2 + c * 8) =
+                    *reinterpret_cast<const dev::u32x4*>(stg + r * big::HSTR + c * 16);
+        }
+    } else {
+        // pair outputs, bf16, staged in two passes of half the tile's columns (fragments
+        // j = 2 pass, 2 pass + 1 of every wave: 128 columns, a 128-byte run per row for each
+        // wave column), then written as whole lines to the rows from the tile's row table
+        uint16_t* o = static_cast<uint16_t*>(a.out);
+        const int32_t* orow = reinterpret_cast<const int32_t*>(lds8 + big::ROWTAB);
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+            for (int i = 0; i < FA; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int col = wn * 64 + jj * 32 + lane % 32;     // staged column
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const int r = wm * big::TM + i * 32 + 8 * (q / 4) + (lane / 32) * 4 + (q % 4);
+                        *reinterpret_cast<uint16_t*>(stg + r * big::HSTR + col * 2) = bf16_bits(acc[i][2 * pass + jj][q]);
+                    }
+                }
+            __syncthreads();
+            // 16 chunks of 16 bytes per staged row: chunks 0-7 are wave column 0's run, 8-15 wave column 1's
+#pragma unroll 4
+            for (int idx = tid; idx < big::BM * 16; idx += big::kThreads) {
+                const int r = idx / 16, c = idx % 16;
+                const int d = orow[r];
+                if (d >= 0)
+                    *reinterpret_cast<dev::u32x4*>(o + int64_t(d) * a.H + t.n0 + (c / 8) * big::TN + pass * 64 + (c % 8) * 8) =
+                        *reinterpret_cast<const dev::u32x4*>(stg + r * big::HSTR + c * 16);
+            }
+            if (pass == 0) __syncthreads();
+        }
+    }
+}
+
+// Persistent: workgroup b serves XCD b % 8 and walks tiles b / 8, b / 8 + G / 8, ... of that
+// XCD's contiguous share of the real tiles (G workgroups in all).
+template <int MODE>
+__global__ void __launch_bounds__(big::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_gemm_big(const GemmArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
+    const int n_tiles = a.N / big::BN;
+    const int total = a.tiles[0] * n_tiles;
+    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const int x = blockIdx.x % kXcds, stride = gridDim.x / kXcds;
+    int i = blockIdx.x / kXcds;
+    if (i >= per_xcd || x * per_xcd + i >= total) return;
+    big::Tile cur = big::make_tile(a, x * per_xcd + i, n_tiles);
+    {
+        const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+        const uint32_t boff = uint32_t(((wave + big::NW * big::QA) * 64 + lane) / big::CPR - big::BM) * uint32_t(a.K) * 2 +
+                              uint32_t(big::lane_chunk()) * 16;
+        big::issue(lds8, a.a_src, cur.ao, cur.bbase, boff, uint32_t(a.K) * 2 * (big::NW * 64 / big::CPR), 0, 0);
+    }
+    while (true) {
+        const int in = i + stride;
+        const bool has_next = in < per_xcd && x * per_xcd + in < total;
+        const big::Tile nx = has_next ? big::make_tile(a, x * per_xcd + in, n_tiles) : cur;
+        switch (cur.fa) {
+            case 4: big_tile<MODE, 4>(a, lds8, cur, nx, has_next); break;
+            case 3: big_tile<MODE, 3>(a, lds8, cur, nx, has_next); break;
+            case 2: big_tile<MODE, 2>(a, lds8, cur, nx, has_next); break;
+            case 1: big_tile<MODE, 1>(a, lds8, cur, nx, has_next); break;
+            default: big_tile<MODE, 0>(a, lds8, cur, nx, has_next); break;
+        }
+        if (!has_next) break;
+        cur = nx;
+        i = in;
+    }
+}
+
 // The GEMM stages use more than the default 64 KiB of LDS per workgroup.
 hipError_t allow_lds() {
     static hipError_t once = [] {
@@ -654,6 +997,11 @@ hipError_t allow_lds() {
         const void* kd[2] = {reinterpret_cast<const void*>(&k_gemm_dma<0>), reinterpret_cast<const void*>(&k_gemm_dma<1>)};
         for (const void* k : kd) {
             hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, dma::kLdsBytes);
+            if (e != hipSuccess) return e;
+        }
+        const void* kb[2] = {reinterpret_cast<const void*>(&k_gemm_big<0>), reinterpret_cast<const void*>(&k_gemm_big<1>)};
+        for (const void* k : kb) {
+            hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, big::kLdsBytes);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
@@ -684,18 +1032,31 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     const WsLayout W = ws_layout(c, T);
     int32_t* tiles = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + W.tiles);
     const bool fp4 = c.w_dtype == MOE_W_MXFP4;
-    const bool dma1 = MOE_GEMM_DMA && !fp4 && (2 * c.inter) % dma::BN == 0 && c.hidden % dma::BK == 0;
-    const bool dma2 = MOE_GEMM_DMA && !fp4 && c.hidden % dma::BN == 0 && c.inter % dma::BK == 0;
+    // kernel per GEMM: 2 large-tile, 1 pipelined 128 x 256, 0 register-staged (MXFP4 and other shapes).
+    // The large tile needs long K loops to pay for its per-tile start and epilogue at one
+    // workgroup per CU (measured on the 8K-token chunk of the 2048 x 768 layer: 572 us against
+    // 653 us for GEMM 1 with K = 2048, but 393 us against 365 us for GEMM 2 with K = 768).
+    auto kind = [&](int N, int K) {
+        if (fp4) return 0;
+        if (K < 2048 && MOE_GEMM_DMA && N % dma::BN == 0 && K % dma::BK == 0) return 1;
+        // an even slice count, and A row offsets (rows of x or h times the row bytes) in 32 bits
+        const int64_t a_rows = int64_t(T) * c.top_k + T;
+        if (MOE_GEMM_BIG && N % big::BN == 0 && K % (2 * big::BK) == 0 && a_rows * K * 2 < (int64_t(1) << 32))
+            return 2;
+        if (MOE_GEMM_DMA && N % dma::BN == 0 && K % dma::BK == 0) return 1;
+        return 0;
+    };
+    auto bm_of = [](int kd) { return kd == 2 ? big::BM : kd == 1 ? dma::BM : BM; };
+    const int kind1 = kind(2 * c.inter, c.hidden), kind2 = kind(c.hidden, c.inter);
     TileMapArgs tm;
     tm.offsets = offsets;
     tm.T = T;
-    tm.bm = dma1 ? dma::BM : BM;
+    tm.bm = bm_of(kind1);
     tm.tiles = tiles;
     tm.list = list;
     hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, s, tm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int mt1 = max_tiles(c, T, tm.bm);
     GemmArgs a;
     a.slot_base = static_cast<const uint8_t*>(slot_base);
     a.shared_blob = static_cast<const uint8_t*>(shared);
@@ -708,6 +1069,44 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     a.I = c.inter;
     a.H = c.hidden;
     a.list = list;
+    if ((e = allow_lds()) != hipSuccess) return e;
+    auto launch = [&](int kd, int mode, int bm) {
+        const int bn = kd == 2 ? big::BN : kd == 1 ? dma::BN : BN;
+        a.grid = (max_tiles(c, T, bm) * (a.N / bn) + kXcds - 1) / kXcds * kXcds;
+        a.mode = mode;
+        if (kd == 2) {
+            // persistent: at most one workgroup per CU (a multiple of the XCD count)
+            static const int n_cu = [] {
+                int dev = 0, n = 0;
+                if (hipGetDevice(&dev) != hipSuccess ||
+                    hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+                    n = 0;
+                return n;
+            }();
+            const int cap = n_cu >= kXcds ? n_cu / kXcds * kXcds : kXcds;
+            a.grid = a.grid < cap ? a.grid : cap;
+            if (mode == 0)
+                hipLaunchKernelGGL((k_gemm_big<0>), dim3(a.grid), dim3(big::kThreads), big::kLdsBytes, s, a);
+            else
+                hipLaunchKernelGGL((k_gemm_big<1>), dim3(a.grid), dim3(big::kThreads), big::kLdsBytes, s, a);
+        } else if (kd == 1) {
+            if (mode == 0)
+                hipLaunchKernelGGL((k_gemm_dma<0>), dim3(a.grid), dim3(dma::kThreads), dma::kLdsBytes, s, a);
+            else
+                hipLaunchKernelGGL((k_gemm_dma<1>), dim3(a.grid), dim3(dma::kThreads), dma::kLdsBytes, s, a);
+        } else if (fp4) {
+            if (mode == 0)
+                hipLaunchKernelGGL((k_gemm<0, true>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
+            else
+                hipLaunchKernelGGL((k_gemm<1, true>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
+        } else {
+            if (mode == 0)
+                hipLaunchKernelGGL((k_gemm<0, false>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
+            else
+                hipLaunchKernelGGL((k_gemm<1, false>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
+        }
+        return hipGetLastError();
+    };
     uint8_t* hbuf = static_cast<uint8_t*>(ws) + W.h;
     // GEMM 1: [rows x H] . [2I x H]^T -> h [rows x I]
     a.off_w = lay.gu;
@@ -716,18 +1115,7 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     a.out = hbuf;
     a.K = c.hidden;
     a.N = 2 * c.inter;
-    if ((e = allow_lds()) != hipSuccess) return e;
-    if (dma1) {
-        a.grid = (mt1 * (a.N / dma::BN) + kXcds - 1) / kXcds * kXcds;
-        hipLaunchKernelGGL((k_gemm_dma<0>), dim3(a.grid), dim3(dma::kThreads), dma::kLdsBytes, s, a);
-    } else {
-        a.grid = (mt1 * (a.N / BN) + kXcds - 1) / kXcds * kXcds;
-        if (fp4)
-            hipLaunchKernelGGL((k_gemm<0, true>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
-        else
-            hipLaunchKernelGGL((k_gemm<0, false>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch(kind1, 0, tm.bm)) != hipSuccess) return e;
     // GEMM 2: h [rows x I] . [H x I]^T -> o [pair rows x H]
     a.off_w = lay.d;
     a.off_s = lay.d_scale;
@@ -735,24 +1123,13 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     a.out = o;
     a.K = c.inter;
     a.N = c.hidden;
-    const int bm2 = dma2 ? dma::BM : BM;
+    const int bm2 = bm_of(kind2);
     if (bm2 != tm.bm) {            // the list is rebuilt after GEMM 1 has read it (same stream)
         tm.bm = bm2;
         hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, s, tm);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int mt2 = max_tiles(c, T, bm2);
-    if (dma2) {
-        a.grid = (mt2 * (a.N / dma::BN) + kXcds - 1) / kXcds * kXcds;
-        hipLaunchKernelGGL((k_gemm_dma<1>), dim3(a.grid), dim3(dma::kThreads), dma::kLdsBytes, s, a);
-    } else {
-        a.grid = (mt2 * (a.N / BN) + kXcds - 1) / kXcds * kXcds;
-        if (fp4)
-            hipLaunchKernelGGL((k_gemm<1, true>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
-        else
-            hipLaunchKernelGGL((k_gemm<1, false>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
-    }
-    return hipGetLastError();
+    return launch(kind2, 1, bm2);
 }
 
 }  // namespace moe
