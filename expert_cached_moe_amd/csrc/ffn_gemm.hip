@@ -657,21 +657,26 @@ __global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
 }
 
 // ---------------------------------------------------------------- large-tile bf16 GEMM
-// 256 x 256 output tiles, 4 waves (2 x 2) of 128 x 128 = 4 x 4 fragments of 32x32x16
-// MFMA.  Per K = 16 a wave reads 8 fragments (8 KiB) from LDS for 16 MFMAs: half the
-// LDS bytes per flop of 64 x 64 wave tiles.  K slices of BK = 64 (128-byte rows, so every
-// row segment a load touches is a whole cache line) are filled by direct global->LDS
-// loads into two 64 KiB stage buffers; with the 256 accumulators in registers this is
-// one workgroup per CU.  The workgroups are persistent: each walks its XCD's share of the
-// tiles, and the first K slice of its next tile is loaded while the current tile's last
-// slice and epilogue run (the epilogue is staged in the LDS above the first buffer), so
-// the per-tile start-up and the output stores overlap the MFMAs.  Waves whose rows lie
-// partly past the expert's last row run only the fragments that hold rows (FA of FM).
+// 256 x 256 output tiles, 8 waves (2 x 4) of 128 x 64 = 4 x 2 fragments of 32x32x16 MFMA,
+// two waves per SIMD (measured on the 8K-token chunk of the 2048 x 768 layer: 547 us for
+// GEMM 1 against 604 us with 4 waves of 128 x 128; a wave that stalls issuing its
+// direct-to-LDS loads leaves the SIMD to the other).  K slices of BK = 64 (128-byte rows,
+// so every row segment a load touches is a whole cache line) are filled by direct
+// global->LDS loads into two 64 KiB stage buffers; the 256 x 256 accumulators fill the
+// register file, so this is one workgroup per CU.  The workgroups are persistent: each
+// walks its XCD's share of the tiles, and the first K slice of its next tile is loaded
+// while the current tile's last slice and epilogue run (the epilogue is staged in the LDS
+// above the first buffer), so the per-tile start-up and the output stores overlap the
+// MFMAs.  Waves whose rows lie partly past the expert's last row run only the fragments
+// that hold rows (FA of FM).
 #ifndef MOE_GEMM_BIG
 #define MOE_GEMM_BIG 1
 #endif
 namespace big {
-constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 2, MF = 32;
+#ifndef MOE_BIG_WN
+#define MOE_BIG_WN 4
+#endif
+constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = MOE_BIG_WN, MF = 32;
 constexpr int NW = WM * WN, kThreads = NW * kWave;
 constexpr int TM = BM / WM, TN = BN / WN, FM = TM / MF, FN = TN / MF;
 constexpr int ROWB = BK * 2, CPR = ROWB / 16;       // 128-byte LDS rows of 8 chunks
@@ -685,7 +690,8 @@ constexpr int kLdsBytes = ROWTAB + BM * 4;
 static_assert(kLdsBytes <= 160 * 1024 && ROWTAB >= 2 * STAGE_BYTES, "LDS per CU; the row table is outside the stages");
 static_assert(Q * NW * 1024 == STAGE_BYTES && QA * NW * 1024 == BM * ROWB, "stage split");
 static_assert(FM * MF == TM && FN * MF == TN && FM == 4, "wave tile (the FA dispatch covers 0..4)");
-static_assert(kThreads == BM, "one output row per thread in the epilogue bookkeeping");
+static_assert(kThreads >= BM, "one output row per thread in the epilogue bookkeeping");
+constexpr int kWavesPerSimd = NW / 4;               // 4 SIMDs per CU, one workgroup per CU
 // chunk c of row r sits at slot c ^ ((r >> 1) & 7): two 128-byte rows share a 256-byte
 // bank window, and the 32 rows of a fragment read land on distinct banks
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
@@ -740,7 +746,7 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& a, int lid, int n_tile
     t.bbase = blob + a.off_w + int64_t(t.n0) * arow_bytes;
     t.obase = (shared ? a.T * a.k : base) + t.m0;
     const int r = tid;                                           // epilogue: tile row tid
-    t.orow = t.m0 + r >= t.rows ? -1 : a.mode == 0 || shared ? t.obase + r : a.perm[base + t.m0 + r];
+    t.orow = r >= BM || t.m0 + r >= t.rows ? -1 : a.mode == 0 || shared ? t.obase + r : a.perm[base + t.m0 + r];
     return t;
 }
 
@@ -832,7 +838,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
     bf16x8 fa0[NA], fb0[big::FN], fa1[NA], fb1[big::FN];
     barrier_loads();            // slice 0 has landed; the previous tile's epilogue is done with the LDS
     big::issue(lds8, a.a_src, t.ao, t.bbase, boff, bstride, big::ROWB, 1);
-    if (MODE == 1) reinterpret_cast<int32_t*>(lds8 + big::ROWTAB)[tid] = t.orow;   // read after later barriers
+    if (MODE == 1 && tid < big::BM) reinterpret_cast<int32_t*>(lds8 + big::ROWTAB)[tid] = t.orow;   // read after later barriers
     if constexpr (FA > 0) frag(lds8, 0, fa0, fb0);
     for (int ks = 0; ks + 1 < nk; ++ks) {
         const uint8_t* as_ = lds8 + (ks & 1) * big::STAGE_BYTES;
@@ -917,8 +923,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
         }
     } else {
         // pair outputs, bf16, staged in two passes of half the tile's columns (fragments
-        // j = 2 pass, 2 pass + 1 of every wave: 128 columns, a 128-byte run per row for each
-        // wave column), then written as whole lines to the rows from the tile's row table
+        // j = FN/2 pass .. FN/2 pass + FN/2 - 1 of every wave: BN/2 columns, a run of TN bytes
+        // per row for each wave column), then written as whole lines to the rows from the
+        // tile's row table
         uint16_t* o = static_cast<uint16_t*>(a.out);
         const int32_t* orow = reinterpret_cast<const int32_t*>(lds8 + big::ROWTAB);
 #pragma unroll
@@ -926,23 +933,25 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
 #pragma unroll
             for (int i = 0; i < FA; ++i)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int col = wn * 64 + jj * 32 + lane % 32;     // staged column
+                for (int jj = 0; jj < big::FN / 2; ++jj) {
+                    const int col = wn * (big::TN / 2) + jj * 32 + lane % 32;     // staged column
 #pragma unroll
                     for (int q = 0; q < 16; ++q) {
                         const int r = wm * big::TM + i * 32 + 8 * (q / 4) + (lane / 32) * 4 + (q % 4);
-                        *reinterpret_cast<uint16_t*>(stg + r * big::HSTR + col * 2) = bf16_bits(acc[i][2 * pass + jj][q]);
+                        *reinterpret_cast<uint16_t*>(stg + r * big::HSTR + col * 2) =
+                            bf16_bits(acc[i][big::FN / 2 * pass + jj][q]);
                     }
                 }
             __syncthreads();
-            // 16 chunks of 16 bytes per staged row: chunks 0-7 are wave column 0's run, 8-15 wave column 1's
+            // 16 chunks of 16 bytes per staged row; wave column w's run is chunks CW w .. CW w + CW - 1
+            constexpr int CW = big::TN / 16;
 #pragma unroll 4
             for (int idx = tid; idx < big::BM * 16; idx += big::kThreads) {
                 const int r = idx / 16, c = idx % 16;
                 const int d = orow[r];
                 if (d >= 0)
-                    *reinterpret_cast<dev::u32x4*>(o + int64_t(d) * a.H + t.n0 + (c / 8) * big::TN + pass * 64 + (c % 8) * 8) =
-                        *reinterpret_cast<const dev::u32x4*>(stg + r * big::HSTR + c * 16);
+                    *reinterpret_cast<dev::u32x4*>(o + int64_t(d) * a.H + t.n0 + (c / CW) * big::TN + pass * (big::TN / 2) +
+                                                   (c % CW) * 8) = *reinterpret_cast<const dev::u32x4*>(stg + r * big::HSTR + c * 16);
             }
             if (pass == 0) __syncthreads();
         }
@@ -952,7 +961,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
 // Persistent: workgroup b serves XCD b % 8 and walks tiles b / 8, b / 8 + G / 8, ... of that
 // XCD's contiguous share of the real tiles (G workgroups in all).
 template <int MODE>
-__global__ void __launch_bounds__(big::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(big::kThreads) __attribute__((amdgpu_waves_per_eu(big::kWavesPerSimd, big::kWavesPerSimd)))
 k_gemm_big(const GemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
     const int n_tiles = a.N / big::BN;
@@ -1034,8 +1043,8 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     const bool fp4 = c.w_dtype == MOE_W_MXFP4;
     // kernel per GEMM: 2 large-tile, 1 pipelined 128 x 256, 0 register-staged (MXFP4 and other shapes).
     // The large tile needs long K loops to pay for its per-tile start and epilogue at one
-    // workgroup per CU (measured on the 8K-token chunk of the 2048 x 768 layer: 572 us against
-    // 653 us for GEMM 1 with K = 2048, but 393 us against 365 us for GEMM 2 with K = 768).
+    // workgroup per CU (measured on the 8K-token chunk of the 2048 x 768 layer: 547 us against
+    // 643 us for GEMM 1 with K = 2048, about even for GEMM 2 with K = 768).
     auto kind = [&](int N, int K) {
         if (fp4) return 0;
         if (K < 2048 && MOE_GEMM_DMA && N % dma::BN == 0 && K % dma::BK == 0) return 1;
