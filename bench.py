@@ -85,7 +85,7 @@ def payload_bytes(wl):
 # sources hash to the value it was taken with.
 DECODE_SOURCES = ("ffn_decode.hip", "ffn_common.h", "device_common.h")
 TRAFFIC = {
-    ("a3b_decode_bf16", 1): {"sha256": "0e9a83a2c709e29e51b80f2ba14e6ee4ed0415381f3daac5c0417152dc76c084",
+    ("a3b_decode_bf16", 1): {"sha256": "4f4b89e5bb716ca89863a08bebea860c34740571c961241c66f7d4b95f5f305c",
                              "fetch_kib": 24608.8 + 12360.5, "write_kib": 48.0 + 32.0},
 }
 FETCH_FACTOR = 262144.0 / 131080.0
