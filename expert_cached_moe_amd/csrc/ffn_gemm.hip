@@ -656,7 +656,7 @@ __global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
     }
 }
 
-// ---------------------------------------------------------------- large-tile bf16 GEMM
+// ---------------------------------------------------------------- large-tile GEMM (bf16 or MXFP4 weights)
 // 256 x 256 output tiles, 8 waves (2 x 4) of 128 x 64 = 4 x 2 fragments of 32x32x16 MFMA,
 // two waves per SIMD (measured on the 8K-token chunk of the 2048 x 768 layer: 547 us for
 // GEMM 1 against 604 us with 4 waves of 128 x 128; a wave that stalls issuing its
@@ -669,6 +669,12 @@ __global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
 // above the first buffer), so the per-tile start-up and the output stores overlap the
 // MFMAs.  Waves whose rows lie partly past the expert's last row run only the fragments
 // that hold rows (FA of FM).
+// MXFP4 weights travel as codes: a slice holds 32 code bytes per weight row (a quarter of
+// bf16), and the tile's e8m0 scales sit in LDS.  The K order inside a slice is permuted the
+// same way for both operands (lane half h, sub-step kk covers K = 32 h + 8 kk .. + 7), so
+// one 16-byte LDS read gives a lane the codes of all four sub-steps and one scale covers
+// them; the codes become bf16 MFMA operands in registers (v_cvt_scalef32_pk_bf16_fp4,
+// exact: every e2m1 value times a power of two fits bf16).
 #ifndef MOE_GEMM_BIG
 #define MOE_GEMM_BIG 1
 #endif
@@ -679,22 +685,35 @@ namespace big {
 constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = MOE_BIG_WN, MF = 32;
 constexpr int NW = WM * WN, kThreads = NW * kWave;
 constexpr int TM = BM / WM, TN = BN / WN, FM = TM / MF, FN = TN / MF;
-constexpr int ROWB = BK * 2, CPR = ROWB / 16;       // 128-byte LDS rows of 8 chunks
-constexpr int STAGE_BYTES = (BM + BN) * ROWB;       // 64 KiB
-constexpr int Q = STAGE_BYTES / 1024 / NW;          // 1 KiB load instructions per wave per slice
-constexpr int QA = BM * ROWB / 1024 / NW;           // the first QA of them load A rows
-constexpr int EPI = STAGE_BYTES;                    // h staging (GEMM 1) starts above buffer 0
-constexpr int HSTR = BN + 16;                       // h staging row: BN/2 bf16 + 16 bytes
-constexpr int ROWTAB = EPI + BM * HSTR;             // output row of each tile row (GEMM 2)
-constexpr int kLdsBytes = ROWTAB + BM * 4;
-static_assert(kLdsBytes <= 160 * 1024 && ROWTAB >= 2 * STAGE_BYTES, "LDS per CU; the row table is outside the stages");
-static_assert(Q * NW * 1024 == STAGE_BYTES && QA * NW * 1024 == BM * ROWB, "stage split");
+constexpr int ROWB = BK * 2, CPR = ROWB / 16;       // A rows (and bf16 weight rows): 128 bytes, 8 chunks
+constexpr int A_BYTES = BM * ROWB;                  // 32 KiB of A per slice
+constexpr int QA = A_BYTES / 1024 / NW;             // 1 KiB A load instructions per wave per slice
+constexpr int HSTR = BN + 16;                       // staging row: BN/2 bf16 + 16 bytes
+constexpr int kMaxKFp4 = 4096;                      // MXFP4: the tile's scales (BM x K/32 bytes) in LDS
+// LDS layout: stage buffers 0 and 1 (A rows, then weight rows), the epilogue staging from
+// buffer 1 up (buffer 0 is taking the next tile's first slice by then), the row table and,
+// for MXFP4, the scales.
+template <bool FP4> struct Lay {
+    static constexpr int BROWB = FP4 ? BK / 2 : BK * 2;   // weight bytes per row and slice
+    static constexpr int STAGE = A_BYTES + BN * BROWB;    // 64 KiB (bf16), 40 KiB (MXFP4)
+    static constexpr int QB = BN * BROWB / 1024 / NW;     // weight load instructions per wave per slice
+    static constexpr int Q = QA + QB;
+    static constexpr int EPI = STAGE;
+    static constexpr int ROWTAB = EPI + BM * HSTR;        // output row of each tile row (GEMM 2)
+    static constexpr int SCALES = ROWTAB + BM * 4;
+    static constexpr int kLdsBytes = FP4 ? SCALES + BM * kMaxKFp4 / 32 : ROWTAB + BM * 4;
+    static_assert(kLdsBytes <= 160 * 1024 && ROWTAB >= 2 * STAGE, "LDS per CU; the row table is outside the stages");
+    static_assert(QB * NW * 1024 == BN * BROWB && QB >= 1, "weight loads split over the waves");
+};
+static_assert(QA * NW * 1024 == A_BYTES, "A loads split over the waves");
 static_assert(FM * MF == TM && FN * MF == TN && FM == 4, "wave tile (the FA dispatch covers 0..4)");
 static_assert(kThreads >= BM, "one output row per thread in the epilogue bookkeeping");
 constexpr int kWavesPerSimd = NW / 4;               // 4 SIMDs per CU, one workgroup per CU
 // chunk c of row r sits at slot c ^ ((r >> 1) & 7): two 128-byte rows share a 256-byte
 // bank window, and the 32 rows of a fragment read land on distinct banks
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+// MXFP4 code rows (32 bytes, 2 chunks): rows r and r + 8 of a 16-row read group are apart
+__device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 3) & 1); }
 
 // One tile as this thread sees it.
 struct Tile {
@@ -702,6 +721,7 @@ struct Tile {
     int obase;                  // output row of tile row 0 when the rows are consecutive (h; shared expert)
     int orow;                   // output row of this thread's tile row (epilogue), -1 past the end
     const uint8_t* bbase;       // weight row n0 at K offset 0 (wave-uniform)
+    const uint8_t* sbase;       // MXFP4: the e8m0 scales of weight row n0 (wave-uniform)
     uint32_t ao[QA];            // byte offsets (from a_src) of the A rows of this lane's QA load chunks
 };
 
@@ -713,6 +733,7 @@ __device__ __forceinline__ int lane_chunk() {
     return swz((wave * 64 + lane) / CPR, lane % CPR);
 }
 
+template <bool FP4>
 __device__ __forceinline__ Tile make_tile(const GemmArgs& a, int lid, int n_tiles) {
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave / WN;
@@ -743,24 +764,63 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& a, int lid, int n_tile
             srow = shared ? a.T * a.k + rr : base + rr;
         t.ao[q] = srow * arow_bytes + c16;
     }
-    t.bbase = blob + a.off_w + int64_t(t.n0) * arow_bytes;
+    t.bbase = blob + a.off_w + int64_t(t.n0) * (FP4 ? a.K / 2 : a.K * 2);
+    t.sbase = blob + a.off_s + int64_t(t.n0) * (a.K / 32);
     t.obase = (shared ? a.T * a.k : base) + t.m0;
     const int r = tid;                                           // epilogue: tile row tid
     t.orow = r >= BM || t.m0 + r >= t.rows ? -1 : a.mode == 0 || shared ? t.obase + r : a.perm[base + t.m0 + r];
     return t;
 }
 
-// Loads of one K slice into stage buffer buf: A rows at a_src + ao[q] + koff, weight rows
-// at bbase + boff + koff (boff: this lane's offset in the tile's weight rows).
+// This lane's byte offset in the tile's weight rows for its first weight load, and the
+// step between its weight loads (QB > 1).  bf16: load QA + q fills chunk (wave + NW (QA + q))
+// * 64 + lane of the stage, weight row that / 8 - BM; MXFP4: load QA fills code chunk
+// wave * 64 + lane, row that / 2.
+template <bool FP4>
+__device__ __forceinline__ uint32_t b_lane_off(int K) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    if (FP4) {
+        const int r = (wave * 64 + lane) / 2;
+        return uint32_t(r) * uint32_t(K / 2) + uint32_t(swz4(r, lane % 2)) * 16;
+    }
+    return uint32_t(((wave + NW * QA) * 64 + lane) / CPR - BM) * uint32_t(K) * 2 + uint32_t(lane_chunk()) * 16;
+}
+template <bool FP4>
+__device__ __forceinline__ uint32_t b_stride(int K) {
+    return FP4 ? 0u : uint32_t(K) * 2 * (NW * 64 / CPR);
+}
+
+// Loads of one K slice into stage buffer buf: A rows at a_src + ao[q] + koa, weight rows at
+// bbase + boff + kob.
+template <bool FP4>
 __device__ __forceinline__ void issue(uint8_t* lds8, const uint8_t* a_src, const uint32_t (&ao)[QA],
-                                      const uint8_t* bbase, uint32_t boff, uint32_t bstride, uint32_t koff, int buf) {
+                                      const uint8_t* bbase, uint32_t boff, uint32_t bstride, uint32_t koa, uint32_t kob,
+                                      int buf) {
     const int wave = threadIdx.x / kWave;
-    uint8_t* st = lds8 + buf * STAGE_BYTES;
+    uint8_t* st = lds8 + buf * Lay<FP4>::STAGE;
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        const uint8_t* src = q < QA ? a_src + (ao[q] + koff) : bbase + (boff + (q - QA) * bstride + koff);
+    for (int q = 0; q < Lay<FP4>::Q; ++q) {
+        const uint8_t* src = q < QA ? a_src + (ao[q] + koa) : bbase + (boff + (q - QA) * bstride + kob);
         __builtin_amdgcn_global_load_lds(src, st + (wave + NW * q) * 1024, 16, 0, 0);
     }
+}
+
+// MXFP4: the tile's scales (BM rows x K/32 bytes, contiguous in the blob) into LDS.
+__device__ __forceinline__ void issue_scales(uint8_t* lds8, const uint8_t* sbase, int K) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int chunks = BM * (K / 32) / 16;               // a multiple of 64 (K a multiple of 128)
+    uint8_t* dst = lds8 + Lay<true>::SCALES;
+    for (int c0 = wave * 64; c0 < chunks; c0 += kThreads)
+        __builtin_amdgcn_global_load_lds(sbase + (c0 + lane) * 16, dst + c0 * 16, 16, 0, 0);
+}
+
+// 8 MXFP4 codes (low nibble first) times the block scale, as bf16 MFMA operands
+__device__ __forceinline__ bf16x8 fp4x8_bf16(uint32_t w, float sc) {
+    const dev::bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+    const dev::bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+    const dev::bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+    const dev::bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+    return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 }  // namespace big
 
@@ -775,15 +835,15 @@ __device__ __forceinline__ void barrier_loads() {
 // One tile for a wave that computes FA fragment rows (0..FM).  On entry the tile's slice 0
 // is in flight into buffer 0; before the last slice the next tile's slice 0 is issued into
 // buffer 0 (for the last tile of the workgroup, a harmless reload of this tile's last slice).
-template <int MODE, int FA>
+template <int MODE, int FA, bool FP4>
 __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const big::Tile& t, const big::Tile& nx,
                                          bool has_next) {
+    using L = big::Lay<FP4>;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave / big::WN, wn = wave % big::WN;
     const int nk = a.K / big::BK;
-    const uint32_t bstride = uint32_t(a.K) * 2 * (big::NW * 64 / big::CPR);   // 32 weight rows
-    const uint32_t boff = uint32_t(((wave + big::NW * big::QA) * 64 + lane) / big::CPR - big::BM) * uint32_t(a.K) * 2 +
-                          uint32_t(big::lane_chunk()) * 16;
+    const uint32_t bstride = big::b_stride<FP4>(a.K);
+    const uint32_t boff = big::b_lane_off<FP4>(a.K);
     constexpr int NA = FA > 0 ? FA : 1;
     f32x16 acc[NA][big::FN];
 #pragma unroll
@@ -793,20 +853,38 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-    // fragments of K sub-step kk (16 wide) of a stage; two register sets, so the reads
-    // of sub-step kk + 1 are in flight while the MFMAs of kk run
-    auto frag = [&](const uint8_t* as_, int kk, bf16x8 (&fa)[NA], bf16x8 (&fb)[big::FN]) {
-        const uint8_t* bs_ = as_ + big::BM * big::ROWB;
-        const int c = kk * 2 + lane / 32;
+    // fragments of K sub-step kk (16 wide) of slice ks in stage as_; two register sets, so
+    // the reads of sub-step kk + 1 are in flight while the MFMAs of kk run.  MXFP4: the
+    // codes and scale of the whole slice are read with sub-step 0 (permuted K order).
+    uint4 bq[big::FN];
+    float bsc[big::FN];
+    auto frag = [&](const uint8_t* as_, int kk, int ks, bf16x8 (&fa)[NA], bf16x8 (&fb)[big::FN]) {
+        const uint8_t* bs_ = as_ + big::A_BYTES;
+        const int c = FP4 ? (lane / 32) * 4 + kk : kk * 2 + lane / 32;
 #pragma unroll
         for (int i = 0; i < FA; ++i) {
             const int R = wm * big::TM + i * 32 + lane % 32;
             fa[i] = *reinterpret_cast<const bf16x8*>(as_ + R * big::ROWB + (big::swz(R, c) << 4));
         }
+        if constexpr (FP4) {
+            if (kk == 0) {
 #pragma unroll
-        for (int j = 0; j < big::FN; ++j) {
-            const int R = wn * big::TN + j * 32 + lane % 32;
-            fb[j] = *reinterpret_cast<const bf16x8*>(bs_ + R * big::ROWB + (big::swz(R, c) << 4));
+                for (int j = 0; j < big::FN; ++j) {
+                    const int R = wn * big::TN + j * 32 + lane % 32;
+                    bq[j] = *reinterpret_cast<const uint4*>(bs_ + R * 32 + (big::swz4(R, lane / 32) << 4));
+                    const uint32_t sc = lds8[L::SCALES + R * (a.K / 32) + ks * 2 + lane / 32];
+                    bsc[j] = sc ? __uint_as_float(sc << 23) : __uint_as_float(0x00400000u);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < big::FN; ++j)
+                fb[j] = big::fp4x8_bf16(kk == 0 ? bq[j].x : kk == 1 ? bq[j].y : kk == 2 ? bq[j].z : bq[j].w, bsc[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < big::FN; ++j) {
+                const int R = wn * big::TN + j * 32 + lane % 32;
+                fb[j] = *reinterpret_cast<const bf16x8*>(bs_ + R * big::ROWB + (big::swz(R, c) << 4));
+            }
         }
     };
     auto mma = [&](const bf16x8 (&fa)[NA], const bf16x8 (&fb)[big::FN]) {
@@ -815,10 +893,12 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
 #pragma unroll
             for (int j = 0; j < big::FN; ++j) acc[i][j] = mfma(fa[i], fb[j], acc[i][j]);
     };
-    // schedule of one sub-step: its MFMAs with the next sub-step's LDS reads placed one
+    // schedule of one sub-step: its MFMAs with the next sub-step's NR LDS reads placed one
     // after each of the first MFMAs
-    constexpr int NR = FA + big::FN, NM = FA * big::FN;
-    auto sched = [&]() {
+    constexpr int NM = FA * big::FN;
+    constexpr int NR_B = FP4 ? 0 : big::FN, NR0 = FA + (FP4 ? 2 * big::FN : big::FN);
+    auto sched = [&](auto nr_) {
+        constexpr int NR = decltype(nr_)::value;
         if constexpr (NM >= NR) {
 #pragma unroll
             for (int n = 0; n < NR; ++n) {
@@ -828,6 +908,8 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
             if constexpr (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
         }
     };
+    using RdK = std::integral_constant<int, FA + NR_B>;   // reads of sub-steps 1..3
+    using Rd0 = std::integral_constant<int, NR0>;         // reads of sub-step 0
 
     // Slice ks is read from buffer ks & 1 (nk is even).  The barrier of slice ks sits
     // before its last sub-step: by then every wave has read all of slice ks (so its buffer
@@ -836,56 +918,62 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
     // sub-step).  The loop body is straight-line and the last slice is peeled, which keeps
     // the accumulators in place across iterations.
     bf16x8 fa0[NA], fb0[big::FN], fa1[NA], fb1[big::FN];
-    barrier_loads();            // slice 0 has landed; the previous tile's epilogue is done with the LDS
-    big::issue(lds8, a.a_src, t.ao, t.bbase, boff, bstride, big::ROWB, 1);
-    if (MODE == 1 && tid < big::BM) reinterpret_cast<int32_t*>(lds8 + big::ROWTAB)[tid] = t.orow;   // read after later barriers
-    if constexpr (FA > 0) frag(lds8, 0, fa0, fb0);
+    barrier_loads();            // slice 0 (and the scales) landed; the previous tile is done with the LDS
+    big::issue<FP4>(lds8, a.a_src, t.ao, t.bbase, boff, bstride, big::ROWB, L::BROWB, 1);
+    if (MODE == 1 && tid < big::BM) reinterpret_cast<int32_t*>(lds8 + L::ROWTAB)[tid] = t.orow;   // read after later barriers
+    if constexpr (FA > 0) frag(lds8, 0, 0, fa0, fb0);
     for (int ks = 0; ks + 1 < nk; ++ks) {
-        const uint8_t* as_ = lds8 + (ks & 1) * big::STAGE_BYTES;
+        const uint8_t* as_ = lds8 + (ks & 1) * L::STAGE;
         if constexpr (FA > 0) {
-            frag(as_, 1, fa1, fb1);
+            frag(as_, 1, ks, fa1, fb1);
             mma(fa0, fb0);
-            frag(as_, 2, fa0, fb0);
+            frag(as_, 2, ks, fa0, fb0);
             mma(fa1, fb1);
-            frag(as_, 3, fa1, fb1);
+            frag(as_, 3, ks, fa1, fb1);
             mma(fa0, fb0);
-            sched();
-            sched();
-            sched();
+            sched(RdK{});
+            sched(RdK{});
+            sched(RdK{});
         }
         barrier_loads();
+        // MXFP4: the next slice's first reads go before the loads that refill this slice's
+        // buffer (in program order, so the code reads are not taken to depend on those
+        // loads); bf16 issues the loads first (measured faster)
+        if constexpr (FA > 0 && FP4) frag(lds8 + ((ks + 1) & 1) * L::STAGE, 0, ks + 1, fa0, fb0);
         {
             // slice ks + 2 into the buffer slice ks leaves; past the end, the next tile's slice 0
             // (or, after the last tile, this tile's last slice again: never read)
             const bool nxt = ks + 2 >= nk;
             const bool other = nxt && has_next;
-            const uint32_t koff = uint32_t(nxt ? (has_next ? 0 : nk - 1) : ks + 2) * big::ROWB;
+            const uint32_t kn = uint32_t(nxt ? (has_next ? 0 : nk - 1) : ks + 2);
             uint32_t ao[big::QA];
 #pragma unroll
             for (int q = 0; q < big::QA; ++q) ao[q] = other ? nx.ao[q] : t.ao[q];
-            big::issue(lds8, a.a_src, ao, other ? nx.bbase : t.bbase, boff, bstride, koff, ks & 1);
+            big::issue<FP4>(lds8, a.a_src, ao, other ? nx.bbase : t.bbase, boff, bstride, kn * big::ROWB, kn * L::BROWB,
+                            ks & 1);
         }
         if constexpr (FA > 0) {
-            frag(lds8 + ((ks + 1) & 1) * big::STAGE_BYTES, 0, fa0, fb0);
+            if constexpr (!FP4) frag(lds8 + ((ks + 1) & 1) * L::STAGE, 0, ks + 1, fa0, fb0);
             mma(fa1, fb1);
-            sched();
+            sched(Rd0{});
         }
     }
     if constexpr (FA > 0) {
-        const uint8_t* as_ = lds8 + big::STAGE_BYTES;       // slice nk - 1 (odd)
-        frag(as_, 1, fa1, fb1);
+        const uint8_t* as_ = lds8 + L::STAGE;       // slice nk - 1 (odd)
+        frag(as_, 1, nk - 1, fa1, fb1);
         mma(fa0, fb0);
-        frag(as_, 2, fa0, fb0);
+        frag(as_, 2, nk - 1, fa0, fb0);
         mma(fa1, fb1);
-        frag(as_, 3, fa1, fb1);
+        frag(as_, 3, nk - 1, fa1, fb1);
         mma(fa0, fb0);
         mma(fa1, fb1);
     }
 
     // Epilogue through the LDS above buffer 0 (buffer 0 is taking the next tile's first
     // slice): the tile is staged there and written out as whole rows, 16 bytes a lane.
-    uint8_t* stg = lds8 + big::EPI;
-    __syncthreads();            // every wave is done with slice nk - 1 (buffer 1)
+    uint8_t* stg = lds8 + L::EPI;
+    __syncthreads();            // every wave is done with slice nk - 1 (buffer 1) and the scales
+    if (FP4 && has_next) big::issue_scales(lds8, nx.sbase, a.K);   // the next tile's, while this one finishes
     if (MODE == 0) {
         // SwiGLU: in a 32-wide fragment lanes 0-15 hold gate and lanes 16-31 up for the
         // same 16 h columns; permlane16_swap of elements q1 and q1+4 hands every lane a
@@ -927,7 +1015,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
         // per row for each wave column), then written as whole lines to the rows from the
         // tile's row table
         uint16_t* o = static_cast<uint16_t*>(a.out);
-        const int32_t* orow = reinterpret_cast<const int32_t*>(lds8 + big::ROWTAB);
+        const int32_t* orow = reinterpret_cast<const int32_t*>(lds8 + L::ROWTAB);
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -960,7 +1048,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
 
 // Persistent: workgroup b serves XCD b % 8 and walks tiles b / 8, b / 8 + G / 8, ... of that
 // XCD's contiguous share of the real tiles (G workgroups in all).
-template <int MODE>
+template <int MODE, bool FP4>
 __global__ void __launch_bounds__(big::kThreads) __attribute__((amdgpu_waves_per_eu(big::kWavesPerSimd, big::kWavesPerSimd)))
 k_gemm_big(const GemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
@@ -970,23 +1058,19 @@ k_gemm_big(const GemmArgs a) {
     const int x = blockIdx.x % kXcds, stride = gridDim.x / kXcds;
     int i = blockIdx.x / kXcds;
     if (i >= per_xcd || x * per_xcd + i >= total) return;
-    big::Tile cur = big::make_tile(a, x * per_xcd + i, n_tiles);
-    {
-        const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-        const uint32_t boff = uint32_t(((wave + big::NW * big::QA) * 64 + lane) / big::CPR - big::BM) * uint32_t(a.K) * 2 +
-                              uint32_t(big::lane_chunk()) * 16;
-        big::issue(lds8, a.a_src, cur.ao, cur.bbase, boff, uint32_t(a.K) * 2 * (big::NW * 64 / big::CPR), 0, 0);
-    }
+    big::Tile cur = big::make_tile<FP4>(a, x * per_xcd + i, n_tiles);
+    big::issue<FP4>(lds8, a.a_src, cur.ao, cur.bbase, big::b_lane_off<FP4>(a.K), big::b_stride<FP4>(a.K), 0, 0, 0);
+    if (FP4) big::issue_scales(lds8, cur.sbase, a.K);
     while (true) {
         const int in = i + stride;
         const bool has_next = in < per_xcd && x * per_xcd + in < total;
-        const big::Tile nx = has_next ? big::make_tile(a, x * per_xcd + in, n_tiles) : cur;
+        const big::Tile nx = has_next ? big::make_tile<FP4>(a, x * per_xcd + in, n_tiles) : cur;
         switch (cur.fa) {
-            case 4: big_tile<MODE, 4>(a, lds8, cur, nx, has_next); break;
-            case 3: big_tile<MODE, 3>(a, lds8, cur, nx, has_next); break;
-            case 2: big_tile<MODE, 2>(a, lds8, cur, nx, has_next); break;
-            case 1: big_tile<MODE, 1>(a, lds8, cur, nx, has_next); break;
-            default: big_tile<MODE, 0>(a, lds8, cur, nx, has_next); break;
+            case 4: big_tile<MODE, 4, FP4>(a, lds8, cur, nx, has_next); break;
+            case 3: big_tile<MODE, 3, FP4>(a, lds8, cur, nx, has_next); break;
+            case 2: big_tile<MODE, 2, FP4>(a, lds8, cur, nx, has_next); break;
+            case 1: big_tile<MODE, 1, FP4>(a, lds8, cur, nx, has_next); break;
+            default: big_tile<MODE, 0, FP4>(a, lds8, cur, nx, has_next); break;
         }
         if (!has_next) break;
         cur = nx;
@@ -1008,9 +1092,16 @@ hipError_t allow_lds() {
             hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, dma::kLdsBytes);
             if (e != hipSuccess) return e;
         }
-        const void* kb[2] = {reinterpret_cast<const void*>(&k_gemm_big<0>), reinterpret_cast<const void*>(&k_gemm_big<1>)};
+        const void* kb[2] = {reinterpret_cast<const void*>(&k_gemm_big<0, false>),
+                             reinterpret_cast<const void*>(&k_gemm_big<1, false>)};
         for (const void* k : kb) {
-            hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, big::kLdsBytes);
+            hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, big::Lay<false>::kLdsBytes);
+            if (e != hipSuccess) return e;
+        }
+        const void* kf[2] = {reinterpret_cast<const void*>(&k_gemm_big<0, true>),
+                             reinterpret_cast<const void*>(&k_gemm_big<1, true>)};
+        for (const void* k : kf) {
+            hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, big::Lay<true>::kLdsBytes);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
@@ -1046,12 +1137,14 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     // workgroup per CU (measured on the 8K-token chunk of the 2048 x 768 layer: 547 us against
     // 643 us for GEMM 1 with K = 2048, about even for GEMM 2 with K = 768).
     auto kind = [&](int N, int K) {
-        if (fp4) return 0;
-        if (K < 2048 && MOE_GEMM_DMA && N % dma::BN == 0 && K % dma::BK == 0) return 1;
-        // an even slice count, and A row offsets (rows of x or h times the row bytes) in 32 bits
+        // large tile: an even slice count, A row offsets (rows of x or h times the row bytes)
+        // in 32 bits and, for MXFP4, the tile's scales within their LDS region
         const int64_t a_rows = int64_t(T) * c.top_k + T;
-        if (MOE_GEMM_BIG && N % big::BN == 0 && K % (2 * big::BK) == 0 && a_rows * K * 2 < (int64_t(1) << 32))
-            return 2;
+        const bool big_ok = MOE_GEMM_BIG && N % big::BN == 0 && K % (2 * big::BK) == 0 &&
+                            a_rows * K * 2 < (int64_t(1) << 32) && (!fp4 || K <= big::kMaxKFp4);
+        if (fp4) return big_ok ? 2 : 0;
+        if (K < 2048 && MOE_GEMM_DMA && N % dma::BN == 0 && K % dma::BK == 0) return 1;
+        if (big_ok) return 2;
         if (MOE_GEMM_DMA && N % dma::BN == 0 && K % dma::BK == 0) return 1;
         return 0;
     };
@@ -1094,10 +1187,14 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
             }();
             const int cap = n_cu >= kXcds ? n_cu / kXcds * kXcds : kXcds;
             a.grid = a.grid < cap ? a.grid : cap;
-            if (mode == 0)
-                hipLaunchKernelGGL((k_gemm_big<0>), dim3(a.grid), dim3(big::kThreads), big::kLdsBytes, s, a);
-            else
-                hipLaunchKernelGGL((k_gemm_big<1>), dim3(a.grid), dim3(big::kThreads), big::kLdsBytes, s, a);
+            const dim3 g(a.grid), b(big::kThreads);
+            if (fp4) {
+                if (mode == 0) hipLaunchKernelGGL((k_gemm_big<0, true>), g, b, big::Lay<true>::kLdsBytes, s, a);
+                else hipLaunchKernelGGL((k_gemm_big<1, true>), g, b, big::Lay<true>::kLdsBytes, s, a);
+            } else {
+                if (mode == 0) hipLaunchKernelGGL((k_gemm_big<0, false>), g, b, big::Lay<false>::kLdsBytes, s, a);
+                else hipLaunchKernelGGL((k_gemm_big<1, false>), g, b, big::Lay<false>::kLdsBytes, s, a);
+            }
         } else if (kd == 1) {
             if (mode == 0)
                 hipLaunchKernelGGL((k_gemm_dma<0>), dim3(a.grid), dim3(dma::kThreads), dma::kLdsBytes, s, a);
