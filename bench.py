@@ -17,7 +17,11 @@ Reported besides ``value``:
                with HIP events around a graph of FFN calls alone that rotate over
                the pool replicas; ``traffic`` is the counter-measured HBM bytes per
                call while the decode kernels are unchanged since the counters;
+               ``warm_r1`` is the same graph on one replica (weights partly served by
+               the last-level cache), reported apart;
   batches      the same step at the other decode batch sizes of the workload;
+  decode_other the same step and FFN roofline on the other decode shapes (hidden 4096,
+               256 experts + 1 shared, top-6; bf16 and MXFP4 weights);
   cpu_baseline the fp64 oracle timed on the host cores on a bounded sample;
   pipeline     the full cached decode step (GPU route -> host plan with q* ->
                PCIe fills on a side stream + CPU experts -> GPU experts -> merge),
@@ -50,6 +54,8 @@ def parse():
     ap.add_argument("--workload", default="a3b_decode_bf16")
     ap.add_argument("--batch", type=int, default=1, help="decode batch of `value`")
     ap.add_argument("--extra-batches", default="4,8", help="further decode batches reported beside `value` ('' for none)")
+    ap.add_argument("--other-decode", default="v4flash_decode_bf16:1,8;v4flash_mxfp4:1,8",
+                    help="further decode workloads with their batches, reported beside `value` ('' for none)")
     ap.add_argument("--replicas", type=int, default=0, help="slot-pool replicas (0: enough to defeat the 256 MB cache)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -170,6 +176,23 @@ def main():
             result["batches"][str(b)] = {k_: e[k_] for k_ in ("tokens_per_s", "ms_per_step", "gpu_experts_per_step",
                                                                "replicas")} | {"roofline": e["roofline"]}
 
+    # ---------------------------------------------------------------- other decode shapes (context)
+    if args.other_decode:
+        result["decode_other"] = {}
+        for item in args.other_decode.split(";"):
+            name, _, bs = item.partition(":")
+            wl2 = synth.workload(name.strip())
+            ex2 = synth.expert_weights_many(wl2, range(wl2.E + wl2.n_shared), threads=16)
+            res = {"hidden": wl2.H, "inter": wl2.I, "experts": wl2.E, "top_k": wl2.k,
+                   "shared_experts": wl2.n_shared, "dtype": wl2.wdtype, "batches": {}}
+            for b in [int(v) for v in bs.split(",") if v.strip()]:
+                with _phase(f"decode {wl2.name} batch {b}"):
+                    e = decode(args, wl2, b, ex2)
+                res["batches"][str(b)] = {k_: e[k_] for k_ in ("tokens_per_s", "ms_per_step", "gpu_experts_per_step",
+                                                                "replicas")} | {"roofline": e["roofline"]}
+            result["decode_other"][wl2.name] = res
+            del ex2
+
     # ---------------------------------------------------------------- 8K prefill chunks (context)
     if not args.no_prefill:
         torch.cuda.empty_cache()
@@ -251,8 +274,8 @@ def decode(args, wl, Bt, experts):
     stream = torch.cuda.Stream()
     h_ids_steps = [np.ascontiguousarray(ids_all[t]) for t in range(n_trace)]
 
-    def ffn(s_idx):
-        t, r = s_idx % n_trace, s_idx % R
+    def ffn(s_idx, rotate=True):
+        t, r = s_idx % n_trace, (s_idx % R if rotate else 0)
         L.ffn(d_x[t * Bt:(t + 1) * Bt], Bt, pools[r], step_experts[t], step_slots[t],
               shared[r] if shared else None, with_shared, torch.cuda.current_stream(), h_ids=h_ids_steps[t])
 
@@ -294,6 +317,8 @@ def decode(args, wl, Bt, experts):
     # is the two kernels' durations back to back.
     n_prof = min(K, 1000)
     ffn_ms = timed_graph(ffn, n_prof)
+    # warm: every call reads replica 0, so weights the last-level cache still holds are reused
+    warm_ms = timed_graph(lambda s_idx: ffn(s_idx, rotate=False), n_prof)
     pairs = Bt * k + (Bt if with_shared else 0)
     ffn_bytes = 0.0
     for s in range(n_prof):
@@ -309,7 +334,9 @@ def decode(args, wl, Bt, experts):
     roofline = {"bound": "hbm", "kernel": "moe_expert_ffn, decode (k_decode_gate_up + k_decode_down)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "ffn_us": round(ffn_ms * 1e3, 3), "bytes_per_launch": round(ffn_bytes), "launches_timed": n_prof}
+                "ffn_us": round(ffn_ms * 1e3, 3), "bytes_per_launch": round(ffn_bytes), "launches_timed": n_prof,
+                "warm_r1": {"ffn_us": round(warm_ms * 1e3, 3),
+                            "achieved": round(ffn_bytes / (warm_ms / 1e3) / 1e9, 1)}}
     log(f"batch {Bt}: {ms_per_step * 1e3:.2f} us/step, {value:.0f} tok/s; FFN {ffn_ms * 1e3:.2f} us, "
         f"{achieved:.0f} GB/s")
     L.close()

@@ -98,6 +98,14 @@ __device__ __forceinline__ float silu_fast(float z) {
 }
 
 
+// Hides a weight chunk from the optimiser at the top of each token iteration, so the
+// MXFP4 decode to bf16 stays inside the token loop: hoisted out of it, the decoded
+// copies hold four times the weight registers live and cut the waves per SIMD.
+template <int WT>
+__device__ __forceinline__ void keep_packed(uint4& w) {
+    if constexpr (WT == WT_FP4) asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+}
+
 // 16-byte weight chunk `ch` of a row, streamed (non-temporal: read once per step).
 __device__ __forceinline__ uint4 load_w(const uint8_t* row, int ch) {
     const dev::u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const dev::u32x4*>(row) + ch);

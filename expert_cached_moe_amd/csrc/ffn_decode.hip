@@ -20,6 +20,8 @@
 // Trick", section "Sparsity Is a Lie": experts are small feed-forward networks).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "ffn_common.h"
 #include "internal.h"
@@ -38,8 +40,43 @@ struct DecodeArgs {
     const uint8_t* act;    // gate/up: x [T][H]; down: h [pair rows][I]
     uint8_t* out;          // gate/up: h; down: o fp32 [pair rows][H]
     int32_t K, nrows, T, k, I, H;
+    int32_t nt;            // MXFP4: activation rows staged in LDS per group
     DecodeList list;
 };
+
+// MXFP4 activations through LDS.  A lane's 16-byte weight chunk holds 32 elements, whose
+// activations are 64 contiguous bytes; read straight from global memory, the four 16-byte
+// pieces of consecutive lanes lie 64 bytes apart, so every load instruction touches four
+// times the cache granules of a dense one, and each wave repeats them.  Instead the
+// workgroup copies each activation row once into LDS with direct-to-LDS loads, stored
+// piece-major: piece i of chunk j at 16-byte slot i*(K/32) + j, so lane reads of piece i
+// for consecutive chunks are consecutive 16-byte slots (measured on MI355X: 3% off the
+// MXFP4 decode FFN).  The copies are issued after the weight loads: fetching the
+// activations first and letting the products start as each weight chunk lands
+// (per-chunk waits) measured 15-20% slower than streaming the weights at once and
+// waiting for everything.
+__device__ __forceinline__ void barrier_loads() {
+    __builtin_amdgcn_s_waitcnt(0);      // vmcnt(0) expcnt(0) lgkmcnt(0): own LDS-bound loads landed
+    __syncthreads();
+}
+
+// Issues the copy of activation row `row` (K bf16 values) into staging slot `slot` of
+// `xs`; K/512 instructions of 64 lanes, spread over the workgroup's nw waves.
+__device__ __forceinline__ void stage_row(uint4* xs, const uint8_t* act, int row, int K, int slot, int wave, int nw,
+                                          int lane) {
+    const int units = K / 8, cpr = K / 32;
+    const uint8_t* src = act + int64_t(row) * K * 2;
+    for (int u = wave; u * kWave < units; u += nw) {
+        const int S = u * kWave + lane, i = S / cpr, j = S - i * cpr;
+        __builtin_amdgcn_global_load_lds(src + 64 * j + 16 * i, xs + slot * units + u * kWave, 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void read_staged(ActChunk<WT_FP4>& av, const uint4* xs, int K, int slot, int chunk) {
+    const int units = K / 8, cpr = K / 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) av.v[i] = xs[slot * units + i * cpr + chunk];
+}
 
 // Pair row and activation row of the i-th set bit of the expert's token mask.
 struct TokenIter {
@@ -58,14 +95,16 @@ struct TokenIter {
 // Rows per wave of the gate/up kernel: small waves keep many loads in flight across
 // the chip (measured on MI355X: one gate+up row pair per wave streams the 50 MB of a
 // 1-token step 20% faster than 8 rows per wave); at least 8 loads per lane.
+// (MXFP4 with 16 loads per lane, or 4 down passes, measured 7-12% slower.)
+constexpr int kGateUpWaves = 4;
 template <int CPL> struct GateUpShape {
     static constexpr int RPW = CPL >= 4 ? 2 : 8 / CPL;  // rows per wave: RPW/2 gate + RPW/2 up
-    static constexpr int WPB = 4;                       // waves per workgroup
+    static constexpr int WPB = kGateUpWaves;            // waves per workgroup
     static constexpr int COLS = RPW / 2 * WPB;          // intermediate columns per workgroup
 };
 
 template <int WT, int CPL>
-__global__ void __launch_bounds__(64 * GateUpShape<CPL>::WPB) k_decode_gate_up(const DecodeArgs a) {
+__global__ void __launch_bounds__(64 * kGateUpWaves) k_decode_gate_up(const DecodeArgs a) {
     constexpr int EPC = Fmt<WT>::EPC;
     constexpr int AB = Fmt<WT>::ABYTES;
     constexpr int RPW = GateUpShape<CPL>::RPW, HALF = RPW / 2, WPB = GateUpShape<CPL>::WPB;
@@ -93,15 +132,19 @@ __global__ void __launch_bounds__(64 * GateUpShape<CPL>::WPB) k_decode_gate_up(c
             sv[q][c] = WT == WT_FP4 ? blob[a.off_s + r * (a.H / 32) + c * kWave + lane] : uint8_t(0);
         }
     }
-    int p, t;
-    while (it.next(p, t)) {
+    // one token: dot products of the wave's rows with x[t], SwiGLU, store h[p]
+    auto token = [&](int p, auto&& act_chunk) {
+#pragma unroll
+        for (int q = 0; q < RPW; ++q)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) keep_packed<WT>(wv[q][c]);
         float part[RPW];
 #pragma unroll
         for (int q = 0; q < RPW; ++q) part[q] = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             ActChunk<WT> av;
-            load_act<WT>(av, a.act + (int64_t(t) * a.H + int64_t(c * kWave + lane) * EPC) * AB);
+            act_chunk(av, c);
 #pragma unroll
             for (int q = 0; q < RPW; ++q) part[q] = chunk_dot<WT>(wv[q][c], av, sv[q][c], part[q]);
         }
@@ -110,6 +153,32 @@ __global__ void __launch_bounds__(64 * GateUpShape<CPL>::WPB) k_decode_gate_up(c
         const float up = __shfl_xor(part[0], 32, kWave);
         if ((lane & 32) == 0 && (lane & (64 / RPW - 1)) == 0)
             store_act<WT>(a.out, int64_t(p) * a.I + col0 + qi, silu(part[0]) * up);
+    };
+    int p, t;
+    if constexpr (WT != WT_FP4) {
+        while (it.next(p, t))
+            token(p, [&](ActChunk<WT>& av, int c) {
+                load_act<WT>(av, a.act + (int64_t(t) * a.H + int64_t(c * kWave + lane) * EPC) * AB);
+            });
+    } else {
+        // groups of up to nt token rows of x, staged after the weight loads are issued; every
+        // wave takes the same token sequence, so the barriers are uniform
+        extern __shared__ __attribute__((aligned(16))) uint4 xs[];
+        bool have = it.next(p, t);
+        while (have) {
+            TokenIter g = it;
+            int gp = p, gt = t, n = 0;
+            for (bool gh = true; n < a.nt && gh; ++n) {
+                stage_row(xs, a.act, gt, a.H, n, wave, WPB, lane);
+                gh = g.next(gp, gt);
+            }
+            barrier_loads();
+            for (int s = 0; s < n; ++s) {
+                token(p, [&](ActChunk<WT>& av, int c) { read_staged(av, xs, a.H, s, c * kWave + lane); });
+                have = it.next(p, t);
+            }
+            __syncthreads();            // group read before the next one lands
+        }
     }
 }
 
@@ -138,7 +207,7 @@ __global__ void __launch_bounds__(64 * kDownWaves) k_decode_down(const DecodeArg
     int p, t;
     bool have = it.next(p, t);
     ActChunk<WT> av0[CPL];
-    if (have) {
+    if (WT != WT_FP4 && have) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) load_act<WT>(av0[c], a.act + (int64_t(p) * a.I + int64_t(c * LPR + lr) * EPC) * AB);
     }
@@ -154,18 +223,19 @@ __global__ void __launch_bounds__(64 * kDownWaves) k_decode_down(const DecodeArg
             sv[q][c] = (WT == WT_FP4 && ok) ? blob[a.off_s + int64_t(r) * (a.I / 32) + c * LPR + lr] : uint8_t(127);
         }
     }
-    bool first = true;
-    while (have) {
+    // one pair row: dot products of the wave's rows with h[p], store o[p]
+    auto token = [&](int p, auto&& act_chunk) {
+#pragma unroll
+        for (int q = 0; q < NPASS; ++q)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) keep_packed<WT>(wv[q][c]);
         float part[NPASS];
 #pragma unroll
         for (int q = 0; q < NPASS; ++q) part[q] = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             ActChunk<WT> av;
-            if (first)
-                av = av0[c];
-            else
-                load_act<WT>(av, a.act + (int64_t(p) * a.I + int64_t(c * LPR + lr) * EPC) * AB);
+            act_chunk(av, c);
 #pragma unroll
             for (int q = 0; q < NPASS; ++q) part[q] = chunk_dot<WT>(wv[q][c], av, sv[q][c], part[q]);
         }
@@ -173,8 +243,30 @@ __global__ void __launch_bounds__(64 * kDownWaves) k_decode_down(const DecodeArg
         const int r = row0 + qi * RPP + g;
         if ((lr & (LPR / NPASS - 1)) == 0 && r < a.nrows)
             store_act<WT>(a.out, int64_t(p) * a.H + r, part[0]);
-        first = false;
-        have = it.next(p, t);
+    };
+    if constexpr (WT != WT_FP4) {
+        if (have) token(p, [&](ActChunk<WT>& av, int c) { av = av0[c]; });
+        while (it.next(p, t))
+            token(p, [&](ActChunk<WT>& av, int c) {
+                load_act<WT>(av, a.act + (int64_t(p) * a.I + int64_t(c * LPR + lr) * EPC) * AB);
+            });
+    } else {
+        // groups of up to nt pair rows of h (uniform over the workgroup, as above)
+        extern __shared__ __attribute__((aligned(16))) uint4 xs[];
+        while (have) {
+            TokenIter gi = it;
+            int gp = p, gt = t, n = 0;
+            for (bool gh = true; n < a.nt && gh; ++n) {
+                stage_row(xs, a.act, gp, a.I, n, wave, kDownWaves, lane);
+                gh = gi.next(gp, gt);
+            }
+            barrier_loads();
+            for (int s = 0; s < n; ++s) {
+                token(p, [&](ActChunk<WT>& av, int c) { read_staged(av, xs, a.I, s, c * LPR + lr); });
+                have = it.next(p, t);
+            }
+            __syncthreads();            // group read before the next one lands
+        }
     }
 }
 
@@ -189,7 +281,8 @@ template <int WT, int CPL>
 hipError_t launch_gu1(const DecodeArgs& a, int n_list, hipStream_t s) {
     using S = GateUpShape<CPL>;
     if (a.I % S::COLS) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_decode_gate_up<WT, CPL>), dim3(a.I / S::COLS, n_list), dim3(64 * S::WPB), 0, s, a);
+    hipLaunchKernelGGL((k_decode_gate_up<WT, CPL>), dim3(a.I / S::COLS, n_list), dim3(64 * S::WPB),
+                       WT == WT_FP4 ? a.nt * a.H * 2 : 0, s, a);
     return hipGetLastError();
 }
 
@@ -210,7 +303,8 @@ hipError_t launch_d(const DecodeArgs& a, int lpr, int cpl, int n_list, hipStream
     const dim3 grid((a.nrows + rpb - 1) / rpb, n_list);
 #define MOE_D(L, C) \
     if (lpr == L && cpl == C) { \
-        hipLaunchKernelGGL((k_decode_down<WT, L, C>), grid, dim3(64 * kDownWaves), 0, s, a); \
+        hipLaunchKernelGGL((k_decode_down<WT, L, C>), grid, dim3(64 * kDownWaves), WT == WT_FP4 ? a.nt * a.I * 2 : 0, \
+                           s, a);                                                                                  \
         return hipGetLastError(); \
     }
 #define MOE_DL(L) MOE_D(L, 1) MOE_D(L, 2) MOE_D(L, 3) MOE_D(L, 4) MOE_D(L, 6) MOE_D(L, 8)
@@ -225,8 +319,18 @@ hipError_t launch_d(const DecodeArgs& a, int lpr, int cpl, int n_list, hipStream
 bool decode_shape_supported(const moe_config& c) {
     const int gu = ffn::chunks_per_row(c.w_dtype, c.hidden), d = ffn::chunks_per_row(c.w_dtype, c.inter);
     int l, cc;
+    // MXFP4 staging copies whole 64-lane instructions: rows of H and I bf16 are multiples of 1 KiB
+    const bool stage_ok = c.w_dtype != MOE_W_MXFP4 || (c.hidden % 512 == 0 && c.inter % 512 == 0);
     return c.inter % 16 == 0 && gu % kWave == 0 && (gu / kWave == 1 || gu / kWave == 2 || gu / kWave == 4 ||
-                                                     gu / kWave == 8) && pick_down(d, &l, &cc);
+                                                     gu / kWave == 8) && pick_down(d, &l, &cc) && stage_ok;
+}
+
+// Activation rows staged per group: the most tokens any listed expert takes, within a
+// 32 KiB LDS budget per workgroup.
+static int staged_rows(const DecodeList& list, int K) {
+    int most = 1;
+    for (int i = 0; i < list.n; ++i) most = std::max(most, __builtin_popcount(list.tokmask[i]));
+    return std::max(1, std::min(most, (32 << 10) / (2 * K)));
 }
 
 hipError_t launch_ffn_decode(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
@@ -245,13 +349,27 @@ hipError_t launch_ffn_decode(const moe_config& c, const BlobLayout& lay, const v
     a.k = c.top_k;
     a.I = c.inter;
     a.H = c.hidden;
-    a.list = list;
+    // Entries with the most tokens first: workgroups start in blockIdx.y order, and an
+    // expert's workgroups take time in proportion to its tokens (the shared expert has all
+    // of them), so last in line they would form the kernel's tail.
+    int order[kMaxDecodeList];
+    for (int i = 0; i < list.n; ++i) order[i] = i;
+    std::stable_sort(order, order + list.n, [&](int x, int y) {
+        return __builtin_popcount(list.tokmask[x]) > __builtin_popcount(list.tokmask[y]);
+    });
+    a.list.n = list.n;
+    for (int i = 0; i < list.n; ++i) {
+        a.list.ent[i] = list.ent[order[i]];
+        a.list.tokmask[i] = list.tokmask[order[i]];
+        a.list.jpack[i] = list.jpack[order[i]];
+    }
     a.off_w = lay.gu;
     a.off_s = lay.gu_scale;
     a.act = static_cast<const uint8_t*>(x);
     a.out = hbuf;
     a.K = c.hidden;
     a.nrows = 2 * c.inter;
+    a.nt = staged_rows(list, c.hidden);
     hipError_t e;
     switch (c.w_dtype) {
         case MOE_W_F32: e = launch_gu<WT_F32>(a, gu_ch / kWave, list.n, s); break;
@@ -265,6 +383,7 @@ hipError_t launch_ffn_decode(const moe_config& c, const BlobLayout& lay, const v
     a.out = static_cast<uint8_t*>(o);
     a.K = c.inter;
     a.nrows = c.hidden;
+    a.nt = staged_rows(list, c.inter);
     switch (c.w_dtype) {
         case MOE_W_F32: return launch_d<WT_F32>(a, lpr, cpld, list.n, s);
         case MOE_W_BF16: return launch_d<WT_BF16>(a, lpr, cpld, list.n, s);

@@ -182,13 +182,15 @@ def test_decode_ffn_merge_parity(B, name, T, frac):
 
 
 @pytest.mark.parametrize("wdtype,H,I,T", [("f32", 512, 256, 1), ("f32", 512, 256, 5), ("bf16", 1024, 512, 1),
-                                          ("bf16", 1024, 512, 8)])
+                                          ("bf16", 1024, 512, 8), ("mxfp4", 2048, 1024, 1), ("mxfp4", 8192, 512, 8)])
 def test_decode_other_shapes(B, wdtype, H, I, T):
     """Decode at hidden/intermediate sizes other than the workloads' (16 experts, top-4):
-    the kernels pick their lanes-per-row and chunks-per-lane from the shape."""
+    the kernels pick their lanes-per-row and chunks-per-lane from the shape.  MXFP4 at
+    hidden 8192 stages two token rows of x per group in LDS, so the shared expert's 8
+    tokens take four groups."""
     print(f"[decode-other-shapes] {wdtype} H={H} I={I} T={T}", flush=True)
     import dataclasses
-    base = synth.workload("tiny_fp32" if wdtype == "f32" else "a3b_decode_bf16")
+    base = synth.workload({"f32": "tiny_fp32", "bf16": "a3b_decode_bf16", "mxfp4": "v4flash_mxfp4"}[wdtype])
     wl = dataclasses.replace(base, name=f"{wdtype}_{H}x{I}", H=H, I=I, E=16, k=4, C=16, batches=(T,))
     _decode_case(B, None, T, 0.75, seed=T + 300, wl=wl)
 
