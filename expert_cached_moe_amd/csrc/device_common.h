@@ -52,8 +52,13 @@ __device__ __forceinline__ int group_reduce_split(float (&v)[NV], int lane) {
 #pragma unroll
             for (int i = 0; i < NV / 2; ++i) {
                 if (i < h) {
-                    const float send = upper ? v[i] : v[i + h];
-                    const float keep = upper ? v[i + h] : v[i];
+                    // both values as registers before the select: a select of the two array
+                    // loads is otherwise folded into a load through a selected address, which
+                    // puts the array in scratch memory
+                    float lo = v[i], hi = v[i + h];
+                    asm("" : "+v"(lo), "+v"(hi));
+                    const float send = upper ? lo : hi;
+                    const float keep = upper ? hi : lo;
                     v[i] = keep + __shfl_xor(send, d, kWave);
                 }
             }

@@ -109,6 +109,10 @@ k_gemv(const GemvArgs a) {
             const int p = shared ? a.T * a.k + i : a.perm[base + i];
             const int arow = GU ? (shared ? i : p / a.k) : p;
             const uint8_t* ap = a.act + int64_t(arow) * act_stride;
+#pragma unroll
+            for (int q = 0; q < NPASS; ++q)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) keep_packed<WT>(wv[q][c]);
             float part[NPASS];
 #pragma unroll
             for (int q = 0; q < NPASS; ++q) part[q] = 0.0f;
