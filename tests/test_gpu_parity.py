@@ -50,7 +50,7 @@ def _route_case(B, wl, logits, renorm=1):
 
 
 @pytest.mark.parametrize("case", ["tiny", "a3b_b1", "a3b_b8", "v4_b8", "prefill_a3b", "prefill_v4", "ragged513",
-                                  "t1", "t0", "ties", "no_renorm", "e8_k8"])
+                                  "t1", "t0", "ties", "no_renorm", "e8_k8", "decode_ties", "decode_no_renorm"])
 def test_route_parity(B, case):
     print(f"[route] {case}", flush=True)
     if case == "tiny":
@@ -93,6 +93,16 @@ def test_route_parity(B, case):
     elif case == "no_renorm":
         wl = synth.workload("v4flash_decode_bf16")
         _route_case(B, wl, synth.iid_logits(wl, 37, tag=3), renorm=0)
+    elif case in ("decode_ties", "decode_no_renorm"):
+        # decode batch sizes (the one-workgroup route and grouping): exact ties, -0 == +0,
+        # and the softmax over all experts
+        wl = synth.workload("a3b_decode_bf16")
+        rng = np.random.default_rng(11)
+        for T in (1, 3, 8):
+            lg = (rng.integers(-3, 3, size=(T, wl.E)) * 0.5).astype(np.float32)
+            lg[:, ::5] = 0.0
+            lg[:, 1::5] = -0.0
+            _route_case(B, wl, lg, renorm=0 if case == "decode_no_renorm" else 1)
     elif case == "e8_k8":
         import dataclasses
         wl = dataclasses.replace(synth.workload("tiny_fp32"), k=8)
