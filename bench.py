@@ -84,15 +84,18 @@ def payload_bytes(wl):
 # HBM traffic of the decode FFN kernels from hardware counters (rocprofv3 --pmc FETCH_SIZE, then
 # --pmc WRITE_SIZE, over `bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-pipeline
 # --prefill-reps 3 --stream-layers 0 --copy-probe`), in KiB per dispatch as the counters read
-# them, summed over k_decode_gate_up and k_decode_down of one moe_expert_ffn call at batch 1
-# (every call has 8 experts).  The same runs read the plain 256 MiB read + 256 MiB write kernel
-# of --copy-probe as FETCH_SIZE 131080 KiB and WRITE_SIZE 262144 KiB, so fetch counts are scaled
-# by 262144 / 131080 and write counts by 1.  A record applies only while the decode kernel
-# sources hash to the value it was taken with.
+# them, averaged over the 100 calls of the rotating FFN graph and summed over k_decode_gate_up
+# and k_decode_down of one moe_expert_ffn call at batch 1 (every call has the same expert
+# count, so the record matches the timed calls).  The same runs read the plain 256 MiB read +
+# 256 MiB write kernel of --copy-probe as FETCH_SIZE 131080 KiB and WRITE_SIZE 262144 KiB, so
+# fetch counts are scaled by 262144 / 131080 and write counts by 1.  A record applies only
+# while the decode kernel sources hash to the value it was taken with.
 DECODE_SOURCES = ("ffn_decode.hip", "ffn_common.h", "device_common.h")
+_SRC = "cbbd45aa992fcee835a63d16c8a75e375881662f696d19637738d1c6b2def220"
 TRAFFIC = {
-    ("a3b_decode_bf16", 1): {"sha256": "4f4b89e5bb716ca89863a08bebea860c34740571c961241c66f7d4b95f5f305c",
-                             "fetch_kib": 24608.8 + 12360.5, "write_kib": 48.0 + 32.0},
+    ("a3b_decode_bf16", 1): {"sha256": _SRC, "fetch_kib": 24612.5 + 12362.0, "write_kib": 48.0 + 32.0},
+    ("v4flash_decode_bf16", 1): {"sha256": _SRC, "fetch_kib": 86071.5 + 43118.5, "write_kib": 84.0 + 56.0},
+    ("v4flash_mxfp4", 1): {"sha256": _SRC, "fetch_kib": 22921.0 + 11546.5, "write_kib": 42.0 + 56.0},
 }
 FETCH_FACTOR = 262144.0 / 131080.0
 WRITE_FACTOR = 1.0
