@@ -2,10 +2,11 @@
 """MoE-layer throughput of the expert-cached layer on one MI355X.
 
 One step = one pass of the layer's GPU path over one decode batch: router
-softmax + top-k and permutation (moe_route), the SwiGLU experts of the step over
-the expert slots (moe_expert_ffn, token lists from the host copy of the step's
-ids, as the cached pipeline has them), and the gate-weighted un-permute and merge
-(moe_merge_partial).  The K timed steps are captured once in a HIP graph and
+softmax + top-k and permutation (moe_route), then the SwiGLU experts of the step over
+the expert slots with the gate-weighted un-permute and merge of their outputs
+(moe_expert_ffn_merge, token lists from the host copy of the step's ids, as the
+cached pipeline has them; bit-identical to moe_expert_ffn + moe_merge_partial, whose
+step time is reported beside it).  The K timed steps are captured once in a HIP graph and
 replayed; inputs (logits, activations, expert slots) are resident in HBM before
 the timed region.  The step's expert set comes from the library's own cache
 planner (moe_lru_replay).  Expert slot pools are replicated R times and the steps
@@ -13,12 +14,15 @@ rotate over the replicas (R emulated layers), so each step's weights come from
 HBM rather than from the 256 MB last-level cache.
 
 Reported besides ``value``:
-  roofline     decode FFN (moe_expert_ffn) algorithmic bytes / time per call, timed
-               with HIP events around a graph of FFN calls alone that rotate over
+  roofline     decode expert FFN (moe_expert_ffn: the HBM-streaming kernels) algorithmic
+               bytes / time per call, timed with HIP events around a graph of those calls alone
+               that rotate over
                the pool replicas; ``traffic`` is the counter-measured HBM bytes per
                call while the decode kernels are unchanged since the counters;
                ``warm_r1`` is the same graph on one replica (weights partly served by
-               the last-level cache), reported apart;
+               the last-level cache), reported apart; ``step_call`` times the call the
+               step makes (moe_expert_ffn_merge: the same gate/up kernel, then down and
+               merge fused) the same way;
   batches      the same step at the other decode batch sizes of the workload;
   decode_other the same step and FFN roofline on the other decode shapes (hidden 4096,
                256 experts + 1 shared, top-6; bf16 and MXFP4 weights);
@@ -168,7 +172,7 @@ def main():
               "config": {"workload": f"{wl.name} decode, batch {Bt}", "hidden": wl.H, "inter": wl.I,
                          "experts": wl.E, "top_k": wl.k, "shared_experts": wl.n_shared, "batch": Bt,
                          "replicas": d["replicas"], "gpu_experts_per_step": d["gpu_experts_per_step"],
-                         "step": "route+permute+ffn+merge, HIP graph"},
+                         "step": "route+permute, then ffn+merge in one call; HIP graph"},
               "roofline": d["roofline"]}
     extra = [int(b) for b in args.extra_batches.split(",") if b.strip()] if args.extra_batches else []
     if extra:
@@ -176,8 +180,9 @@ def main():
         for b in extra:
             with _phase(f"decode batch {b}"):
                 e = decode(args, wl, b, experts)
-            result["batches"][str(b)] = {k_: e[k_] for k_ in ("tokens_per_s", "ms_per_step", "gpu_experts_per_step",
-                                                               "replicas")} | {"roofline": e["roofline"]}
+            result["batches"][str(b)] = {k_: e[k_] for k_ in ("tokens_per_s", "ms_per_step", "two_calls_ms_per_step",
+                                                               "gpu_experts_per_step", "replicas")} | \
+                {"roofline": e["roofline"]}
 
     # ---------------------------------------------------------------- other decode shapes (context)
     if args.other_decode:
@@ -191,8 +196,9 @@ def main():
             for b in [int(v) for v in bs.split(",") if v.strip()]:
                 with _phase(f"decode {wl2.name} batch {b}"):
                     e = decode(args, wl2, b, ex2)
-                res["batches"][str(b)] = {k_: e[k_] for k_ in ("tokens_per_s", "ms_per_step", "gpu_experts_per_step",
-                                                                "replicas")} | {"roofline": e["roofline"]}
+                res["batches"][str(b)] = {k_: e[k_] for k_ in ("tokens_per_s", "ms_per_step", "two_calls_ms_per_step",
+                                                                "gpu_experts_per_step", "replicas")} | \
+                    {"roofline": e["roofline"]}
             result["decode_other"][wl2.name] = res
             del ex2
 
@@ -277,16 +283,30 @@ def decode(args, wl, Bt, experts):
     stream = torch.cuda.Stream()
     h_ids_steps = [np.ascontiguousarray(ids_all[t]) for t in range(n_trace)]
 
+    def ffn_merge(s_idx, rotate=True):
+        """The step's experts and the merge of their outputs (moe_expert_ffn_merge)."""
+        t, r = s_idx % n_trace, (s_idx % R if rotate else 0)
+        L.ffn_merge(d_x[t * Bt:(t + 1) * Bt], Bt, pools[r], step_experts[t], step_slots[t], h_ids_steps[t],
+                    shared[r] if shared else None, with_shared, None, out, torch.cuda.current_stream())
+
     def ffn(s_idx, rotate=True):
+        """The step's experts alone (moe_expert_ffn: the pair outputs)."""
         t, r = s_idx % n_trace, (s_idx % R if rotate else 0)
         L.ffn(d_x[t * Bt:(t + 1) * Bt], Bt, pools[r], step_experts[t], step_slots[t],
               shared[r] if shared else None, with_shared, torch.cuda.current_stream(), h_ids=h_ids_steps[t])
 
     def enqueue(s_idx):
         t = s_idx % n_trace
+        L.route(d_logits[t * Bt:(t + 1) * Bt], Bt, torch.cuda.current_stream())
+        ffn_merge(s_idx)
+
+    def enqueue_two_calls(s_idx):
+        """The same step through moe_expert_ffn (pair outputs) and moe_merge_partial."""
+        t, r = s_idx % n_trace, s_idx % R
         st = torch.cuda.current_stream()
         L.route(d_logits[t * Bt:(t + 1) * Bt], Bt, st)
-        ffn(s_idx)
+        L.ffn(d_x[t * Bt:(t + 1) * Bt], Bt, pools[r], step_experts[t], step_slots[t],
+              shared[r] if shared else None, with_shared, st, h_ids=h_ids_steps[t])
         L.merge(step_experts[t], with_shared, None, Bt, out, st)
 
     def timed_graph(body, n):
@@ -315,20 +335,25 @@ def decode(args, wl, Bt, experts):
     value = Bt / (ms_per_step / 1e3)
 
     # ---------------------------------------------------------------- decode FFN roofline
-    # The FFN calls of n_prof consecutive steps alone in one graph: each call reads its
-    # experts from the next pool replica, so the weights come from HBM, and the per-call time
-    # is the two kernels' durations back to back.
+    two_calls_ms = timed_graph(enqueue_two_calls, K)
+
+    # The expert FFN calls (moe_expert_ffn: the HBM-streaming kernels) of n_prof consecutive
+    # steps alone in one graph: each call reads its experts from the next pool replica, so the
+    # weights come from HBM, and the per-call time is the two kernels' durations back to back.
+    # The step itself runs the same gate/up kernel, then down and merge fused (timed apart).
     n_prof = min(K, 1000)
     ffn_ms = timed_graph(ffn, n_prof)
     # warm: every call reads replica 0, so weights the last-level cache still holds are reused
     warm_ms = timed_graph(lambda s_idx: ffn(s_idx, rotate=False), n_prof)
+    fused_ms = timed_graph(ffn_merge, n_prof)
     pairs = Bt * k + (Bt if with_shared else 0)
-    ffn_bytes = 0.0
+    act = 2 if wl.act_dtype == "bf16" else 4
+    w_bytes = 0.0
     for s in range(n_prof):
-        ne = len(step_experts[(W + s) % n_trace])
-        act = 2 if wl.act_dtype == "bf16" else 4
-        ffn_bytes += (ne + with_shared) * payload_bytes(wl) + Bt * H * act + pairs * H * act
-    ffn_bytes /= n_prof
+        w_bytes += (len(step_experts[(W + s) % n_trace]) + with_shared) * payload_bytes(wl)
+    w_bytes /= n_prof
+    ffn_bytes = w_bytes + Bt * H * act + pairs * H * act              # weights, x, pair outputs
+    fused_bytes = w_bytes + Bt * H * act + Bt * H * act + pairs * 8   # weights, x, layer output, gates
     achieved = ffn_bytes / (ffn_ms / 1e3) / 1e9
     rec = TRAFFIC.get((wl.name, Bt))
     traffic = None
@@ -339,13 +364,18 @@ def decode(args, wl, Bt, experts):
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "ffn_us": round(ffn_ms * 1e3, 3), "bytes_per_launch": round(ffn_bytes), "launches_timed": n_prof,
                 "warm_r1": {"ffn_us": round(warm_ms * 1e3, 3),
-                            "achieved": round(ffn_bytes / (warm_ms / 1e3) / 1e9, 1)}}
+                            "achieved": round(ffn_bytes / (warm_ms / 1e3) / 1e9, 1)},
+                "step_call": {"call": "moe_expert_ffn_merge (k_decode_gate_up + k_decode_down_merge when the "
+                                      "list has at most 8 entries, else + k_decode_down + k_merge)",
+                              "us": round(fused_ms * 1e3, 3), "bytes_per_launch": round(fused_bytes),
+                              "achieved": round(fused_bytes / (fused_ms / 1e3) / 1e9, 1)}}
     log(f"batch {Bt}: {ms_per_step * 1e3:.2f} us/step, {value:.0f} tok/s; FFN {ffn_ms * 1e3:.2f} us, "
         f"{achieved:.0f} GB/s")
     L.close()
     del pools, shared, d_logits, d_x
     torch.cuda.empty_cache()
     return {"tokens_per_s": round(value, 1), "ms_per_step": round(ms_per_step, 5), "replicas": R,
+            "two_calls_ms_per_step": round(two_calls_ms, 5),
             "gpu_experts_per_step": round(mean_distinct, 3), "roofline": roofline,
             "logits": logits, "x": x, "w_dtype": dt}
 

@@ -34,6 +34,7 @@ EXPORTS = [
     "moe_workspace_bytes", "moe_pair_rows", "moe_pack_expert", "moe_bind_pools", "moe_route",
     "moe_qstar", "moe_lru_step", "moe_lru_replay", "moe_lru_reset", "moe_lru_slots", "moe_lru_stats",
     "moe_fill", "moe_fill_wait", "moe_upload", "moe_expert_ffn", "moe_host_ffn", "moe_merge_partial",
+    "moe_expert_ffn_merge",
     "moe_prefill_stream", "moe_router_logits", "moe_lru_resize", "moe_move_slots",
 ]
 
@@ -94,6 +95,8 @@ _sig = {
     "moe_host_ffn": (ctypes.c_int, [vp, vp, ctypes.c_int32, vp, vp, _P(moe_plan), vp, ctypes.c_int32]),
     "moe_merge_partial": (ctypes.c_int, [vp, vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, vp,
                                          ctypes.c_int32, vp, vp]),
+    "moe_expert_ffn_merge": (ctypes.c_int, [vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp,
+                                            ctypes.c_int32, vp, vp, vp, vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -319,6 +322,18 @@ def moe_merge_partial(ctx, d_o, d_topk_ids, d_topk_w, h_gpu_experts, n_gpu, with
     ge = np.ascontiguousarray(h_gpu_experts, dtype=np.int32) if h_gpu_experts is not None else None
     _check(ctx, _lib.moe_merge_partial(ctx, _ptr(d_o), _ptr(d_topk_ids), _ptr(d_topk_w), _ptr(ge), n_gpu,
                                        with_shared, _ptr(d_y_host), T, _ptr(d_out), _stream(s)))
+
+
+def moe_expert_ffn_merge(ctx, d_x, T, h_topk_ids, d_topk_ids, d_topk_w, d_slot_base, h_experts, h_slots, n,
+                         d_shared, with_shared, d_y_host, d_out, d_ws, s=None) -> None:
+    he = np.ascontiguousarray(h_experts, dtype=np.int32) if h_experts is not None else None
+    hs = np.ascontiguousarray(h_slots, dtype=np.int32) if h_slots is not None else None
+    hi = h_topk_ids
+    if isinstance(hi, np.ndarray):
+        hi = np.ascontiguousarray(hi, dtype=np.int32)
+    _check(ctx, _lib.moe_expert_ffn_merge(ctx, _ptr(d_x), T, _ptr(hi), _ptr(d_topk_ids), _ptr(d_topk_w),
+                                          _ptr(d_slot_base), _ptr(he), _ptr(hs), n, _ptr(d_shared), with_shared,
+                                          _ptr(d_y_host), _ptr(d_out), _ptr(d_ws), _stream(s)))
 
 
 def moe_prefill_stream(ctx, d_layer_bufs, n_buffers, d_logits, d_x, T, d_shared, d_topk_ids, d_topk_w, d_counts,

@@ -73,7 +73,11 @@ WsLayout ws_layout(const moe_config& c, int32_t max_T) {
     W.base = align256(W.hist + chunks * c.n_experts * 4);
     W.tiles = align256(W.base + chunks * c.n_experts * 4);
     W.h = align256(W.tiles + gemm_tile_ints(c, int32_t(T)) * 4);
-    W.bytes = align256(W.h + rows * int64_t(c.inter) * act_bytes(c));
+    // pair outputs of moe_expert_ffn_merge when it does not fuse (decode batches only)
+    const int64_t Td = T < kDecodeMaxT ? T : kDecodeMaxT;
+    const int64_t rows_d = Td * c.top_k + (c.n_shared ? Td : 0);
+    W.o = align256(W.h + rows * int64_t(c.inter) * act_bytes(c));
+    W.bytes = align256(W.o + rows_d * int64_t(c.hidden) * act_bytes(c));
     return W;
 }
 
@@ -295,6 +299,38 @@ int moe_fill_wait(moe_ctx* ctx, hipStream_t s) {
     return e == hipSuccess ? MOE_OK : hip_fail(ctx, e, "hipStreamWaitEvent");
 }
 
+// Decode expert list from the host's copy of the top-k ids: per listed expert its tokens
+// (bit t) and each token's slot j among its k picks; the shared expert (last) takes all.
+// where[e] = index of expert e in h_experts or -1.
+static int build_decode_list(moe_ctx* ctx, int32_t T, const int32_t* h_topk_ids, const int32_t* h_experts,
+                             const int32_t* h_slots, int32_t n, int32_t with_shared, const std::vector<int32_t>& where,
+                             DecodeList* dl) {
+    const moe_config& c = ctx->cfg;
+    dl->n = n + (with_shared ? 1 : 0);
+    for (int i = 0; i < n; ++i) {
+        dl->ent[i] = h_experts[i] | (h_slots[i] << 10);
+        dl->tokmask[i] = 0;
+        dl->jpack[i] = 0;
+    }
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < c.top_k; ++j) {
+            const int id = h_topk_ids[t * c.top_k + j];
+            if (id < 0 || id >= c.n_experts) return fail(ctx, MOE_EINVAL, "top-k id out of range");
+            for (int jj = 0; jj < j; ++jj)
+                if (h_topk_ids[t * c.top_k + jj] == id) return fail(ctx, MOE_EINVAL, "repeated expert in a token");
+            const int i = where[id];
+            if (i < 0) continue;
+            dl->tokmask[i] |= 1u << t;
+            dl->jpack[i] |= uint32_t(j) << (4 * t);
+        }
+    if (with_shared) {
+        dl->ent[n] = kSharedTag;
+        dl->tokmask[n] = (1u << T) - 1u;
+        dl->jpack[n] = 0;
+    }
+    return MOE_OK;
+}
+
 int moe_expert_ffn(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* h_topk_ids, const int32_t* d_offsets,
                    const int32_t* d_perm, const void* d_slot_base, const int32_t* h_experts, const int32_t* h_slots,
                    int32_t n, const void* d_shared, int32_t with_shared, void* d_o, void* d_ws, hipStream_t s) {
@@ -319,28 +355,8 @@ int moe_expert_ffn(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* h_to
     hipError_t e;
     if (host_lists) {
         DecodeList dl;
-        dl.n = n + (with_shared ? 1 : 0);
-        for (int i = 0; i < n; ++i) {
-            dl.ent[i] = h_experts[i] | (h_slots[i] << 10);
-            dl.tokmask[i] = 0;
-            dl.jpack[i] = 0;
-        }
-        for (int t = 0; t < T; ++t)
-            for (int j = 0; j < c.top_k; ++j) {
-                const int id = h_topk_ids[t * c.top_k + j];
-                if (id < 0 || id >= c.n_experts) return fail(ctx, MOE_EINVAL, "top-k id out of range");
-                for (int jj = 0; jj < j; ++jj)
-                    if (h_topk_ids[t * c.top_k + jj] == id) return fail(ctx, MOE_EINVAL, "repeated expert in a token");
-                const int i = where[id];
-                if (i < 0) continue;
-                dl.tokmask[i] |= 1u << t;
-                dl.jpack[i] |= uint32_t(j) << (4 * t);
-            }
-        if (with_shared) {
-            dl.ent[n] = kSharedTag;
-            dl.tokmask[n] = (1u << T) - 1u;
-            dl.jpack[n] = 0;
-        }
+        const int st = build_decode_list(ctx, T, h_topk_ids, h_experts, h_slots, n, with_shared, where, &dl);
+        if (st != MOE_OK) return st;
         e = launch_ffn_decode(c, ctx->lay, d_x, T, d_slot_base, d_shared, dl, d_o, d_ws, s);
         return e == hipSuccess ? MOE_OK : hip_fail(ctx, e, "moe_expert_ffn launch");
     }
@@ -355,6 +371,39 @@ int moe_expert_ffn(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* h_to
         e = launch_ffn_gemm(c, ctx->lay, d_x, T, d_offsets, d_perm, d_slot_base, d_shared, list, d_o, d_ws, s);
     }
     return e == hipSuccess ? MOE_OK : hip_fail(ctx, e, "moe_expert_ffn launch");
+}
+
+int moe_expert_ffn_merge(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* h_topk_ids,
+                         const int32_t* d_topk_ids, const float* d_topk_w, const void* d_slot_base,
+                         const int32_t* h_experts, const int32_t* h_slots, int32_t n, const void* d_shared,
+                         int32_t with_shared, const float* d_y_host, void* d_out, void* d_ws, hipStream_t s) {
+    if (!ctx) return MOE_EINVAL;
+    const moe_config& c = ctx->cfg;
+    if (T < 0) return fail(ctx, MOE_EINVAL, "T < 0");
+    if (n < 0 || n > c.n_experts) return fail(ctx, MOE_EINVAL, "n must be in 0..E");
+    if (with_shared != 0 && with_shared != 1) return fail(ctx, MOE_EINVAL, "with_shared must be 0 or 1");
+    if (with_shared && (!c.n_shared || !d_shared)) return fail(ctx, MOE_EINVAL, "no shared expert");
+    if (T == 0) return MOE_OK;
+    if (T > kDecodeMaxT || !decode_shape_supported(c))
+        return fail(ctx, MOE_ESHAPE, "moe_expert_ffn_merge takes decode batches (T <= 8) of the decode shapes");
+    if (!d_x || !d_out || !d_ws || !h_topk_ids || !d_topk_ids || !d_topk_w)
+        return fail(ctx, MOE_EINVAL, "null x/out/workspace/top-k argument");
+    if (n > 0 && (!h_experts || !h_slots || !d_slot_base)) return fail(ctx, MOE_EINVAL, "null routed-expert argument");
+    std::vector<int32_t> where(c.n_experts, -1);
+    uint32_t mask[kMaxExperts / 32] = {0};
+    for (int i = 0; i < n; ++i) {
+        const int e = h_experts[i], sl = h_slots[i];
+        if (e < 0 || e >= c.n_experts || where[e] >= 0) return fail(ctx, MOE_EINVAL, "expert id out of range or repeated");
+        if (sl < 0 || sl >= (1 << 21)) return fail(ctx, MOE_EINVAL, "slot out of range");
+        where[e] = i;
+        mask[e >> 5] |= 1u << (e & 31);
+    }
+    DecodeList dl;
+    const int st = build_decode_list(ctx, T, h_topk_ids, h_experts, h_slots, n, with_shared, where, &dl);
+    if (st != MOE_OK) return st;
+    hipError_t e = launch_ffn_decode_merge(c, ctx->lay, d_x, T, d_slot_base, d_shared, dl, d_topk_ids, d_topk_w, mask,
+                                           with_shared, d_y_host, d_out, d_ws, s);
+    return e == hipSuccess ? MOE_OK : hip_fail(ctx, e, "moe_expert_ffn_merge launch");
 }
 
 int moe_merge_partial(moe_ctx* ctx, const void* d_o, const int32_t* d_topk_ids, const float* d_topk_w,

@@ -32,6 +32,16 @@ namespace {
 using dev::kWave;
 using namespace ffn;
 
+// Layer output of the fused down + merge kernel (the arguments of moe_merge_partial).
+struct MergeTarget {
+    const int32_t* ids;    // device top-k ids [T][k]
+    const float* w;        // device gates [T][k]
+    const float* y_host;   // host-expert partial sums, fp32 [T][H], or null
+    void* out;             // [T][H]: bf16 (bf16 and MXFP4 weights) or fp32
+    uint32_t mask[kMaxExperts / 32];  // experts whose pair outputs count
+    int32_t with_shared;
+};
+
 struct DecodeArgs {
     const uint8_t* slot_base;
     const uint8_t* shared_blob;
@@ -41,6 +51,7 @@ struct DecodeArgs {
     uint8_t* out;          // gate/up: h; down: o fp32 [pair rows][H]
     int32_t K, nrows, T, k, I, H;
     int32_t nt;            // MXFP4: activation rows staged in LDS per group
+    MergeTarget m;         // fused down + merge: gates, mask and layer output
     DecodeList list;
 };
 
@@ -270,6 +281,120 @@ __global__ void __launch_bounds__(64 * kDownWaves) k_decode_down(const DecodeArg
     }
 }
 
+// Down projection and gate-weighted merge in one launch.  A workgroup owns RPW rows of the
+// output for every listed expert: wave w computes the pair outputs of entries w, w + 8, ...
+// for those rows exactly as k_decode_down does (same lanes, chunks and reduction order),
+// rounds them to the activation dtype and keeps them in LDS; after one barrier each
+// (token, row) is merged exactly as k_merge does: gate-weighted pair outputs of the GPU
+// experts in order j = 0..k-1 (fmaf), then the shared expert's row, then the host part.
+// The result is therefore bit-identical to moe_expert_ffn followed by moe_merge_partial,
+// without the pair outputs going through memory or a third launch.  Used when the list
+// has at most one entry per wave (decode at batch 1 of the workloads' shapes: 7-8 experts).
+constexpr int kFusedWaves = 8, kFusedTopK = 8;
+
+template <int WT, int LPR, int CPL>
+__global__ void __launch_bounds__(64 * kFusedWaves) k_decode_down_merge(const DecodeArgs a) {
+    constexpr int EPC = Fmt<WT>::EPC;
+    constexpr int AB = Fmt<WT>::ABYTES;
+    constexpr int RPP = kWave / LPR;
+    constexpr int NPASS = kDownPasses;
+    constexpr int RPW = NPASS * RPP;
+    static_assert(NPASS <= LPR && RPW <= 8, "pass layout");
+    __shared__ float s_o[(kDecodeMaxT * kFusedTopK + kDecodeMaxT) * RPW];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int g = lane / LPR, lr = lane % LPR;
+    const int64_t row_bytes = Fmt<WT>::row_bytes(a.I);
+    const int row0 = blockIdx.x * RPW;
+    // the merge's ids, gates and host part, issued first so their latency hides under the
+    // weight stream (thread i < T*RPW merges token i / RPW, row i % RPW; the loads are
+    // unconditional, at index 0 for the other threads, so none waits behind a branch)
+    const bool merger = tid < a.T * RPW;
+    const int mt = merger ? tid / RPW : 0, mrl = tid % RPW, mrow = row0 + mrl;
+    int mid[kFusedTopK];
+    float mw[kFusedTopK];
+#pragma unroll
+    for (int j = 0; j < kFusedTopK; ++j) {
+        const int pj = merger && j < a.k ? mt * a.k + j : 0;
+        mid[j] = a.m.ids[pj];
+        mw[j] = a.m.w[pj];
+    }
+    float myh = 0.0f;
+    if (a.m.y_host) myh = a.m.y_host[int64_t(mt) * a.H + (mrow < a.H ? mrow : 0)];
+    for (int ei = wave; ei < a.list.n; ei += kFusedWaves) {
+        const int entry = a.list.ent[ei];
+        const bool shared = (entry & 1023) == kSharedTag;
+        const uint8_t* blob = shared ? a.shared_blob : a.slot_base + int64_t(entry >> 10) * a.blob_bytes;
+        TokenIter it{a.list.tokmask[ei], a.list.jpack[ei], shared, a.T, a.k};
+        int p, t;
+        bool have = it.next(p, t);
+        // first token's h prefetched ahead of the weights (not for MXFP4: 64 bytes per chunk)
+        ActChunk<WT> av0[WT == WT_FP4 ? 1 : CPL];
+        if (WT != WT_FP4 && have) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                load_act<WT>(av0[c], a.act + (int64_t(p) * a.I + int64_t(c * LPR + lr) * EPC) * AB);
+        }
+        uint4 wv[NPASS][CPL];
+        uint8_t sv[NPASS][CPL];
+#pragma unroll
+        for (int q = 0; q < NPASS; ++q) {
+            const int r = row0 + q * RPP + g;
+            const bool ok = r < a.nrows;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                wv[q][c] = ok ? load_w(blob + a.off_w + int64_t(r) * row_bytes, c * LPR + lr) : make_uint4(0, 0, 0, 0);
+                sv[q][c] = (WT == WT_FP4 && ok) ? blob[a.off_s + int64_t(r) * (a.I / 32) + c * LPR + lr] : uint8_t(127);
+            }
+        }
+        auto token = [&](int p, auto&& act_chunk) {
+#pragma unroll
+            for (int q = 0; q < NPASS; ++q)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) keep_packed<WT>(wv[q][c]);
+            float part[NPASS];
+#pragma unroll
+            for (int q = 0; q < NPASS; ++q) part[q] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                ActChunk<WT> av;
+                act_chunk(av, c);
+#pragma unroll
+                for (int q = 0; q < NPASS; ++q) part[q] = chunk_dot<WT>(wv[q][c], av, sv[q][c], part[q]);
+            }
+            const int qi = dev::group_reduce_split<NPASS, LPR>(part, lane);
+            if ((lr & (LPR / NPASS - 1)) == 0)   // the value a pair-output store would write, read back
+                s_o[p * RPW + qi * RPP + g] =
+                    WT == WT_F32 ? part[0] : __uint_as_float(uint32_t(dev::f32_to_bf16_bits(part[0])) << 16);
+        };
+        if (WT != WT_FP4 && have) token(p, [&](ActChunk<WT>& av, int c) { av = av0[WT == WT_FP4 ? 0 : c]; });
+        else if (have)
+            token(p, [&](ActChunk<WT>& av, int c) {
+                load_act<WT>(av, a.act + (int64_t(p) * a.I + int64_t(c * LPR + lr) * EPC) * AB);
+            });
+        while (it.next(p, t))
+            token(p, [&](ActChunk<WT>& av, int c) {
+                load_act<WT>(av, a.act + (int64_t(p) * a.I + int64_t(c * LPR + lr) * EPC) * AB);
+            });
+    }
+    __syncthreads();
+    if (merger && mrow < a.H) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kFusedTopK; ++j) {
+            const int e = mid[j];
+            if (j < a.k && ((a.m.mask[e >> 5] >> (e & 31)) & 1u))
+                acc = fmaf(mw[j], s_o[(mt * a.k + j) * RPW + mrl], acc);
+        }
+        const float sh = a.m.with_shared ? s_o[(a.T * a.k + mt) * RPW + mrl] : 0.0f;
+        acc += sh;
+        acc += myh;
+        if (WT == WT_F32)
+            static_cast<float*>(a.m.out)[int64_t(mt) * a.H + mrow] = acc;
+        else
+            static_cast<uint16_t*>(a.m.out)[int64_t(mt) * a.H + mrow] = uint16_t(dev::pack_bf16x2(acc, 0.0f));
+    }
+}
+
 bool pick_down(int d_ch, int* lpr, int* cpl) {
     for (int l : {64, 32, 16})
         for (int c : {1, 2, 3, 4, 6, 8})
@@ -314,6 +439,22 @@ hipError_t launch_d(const DecodeArgs& a, int lpr, int cpl, int n_list, hipStream
     return hipErrorInvalidValue;
 }
 
+template <int WT>
+hipError_t launch_dm(const DecodeArgs& a, int lpr, int cpl, hipStream_t s) {
+    const int rpw = kDownPasses * (kWave / lpr);
+    const dim3 grid((a.nrows + rpw - 1) / rpw);
+#define MOE_DM(L, C) \
+    if (lpr == L && cpl == C) { \
+        hipLaunchKernelGGL((k_decode_down_merge<WT, L, C>), grid, dim3(64 * kFusedWaves), 0, s, a); \
+        return hipGetLastError(); \
+    }
+#define MOE_DML(L) MOE_DM(L, 1) MOE_DM(L, 2) MOE_DM(L, 3) MOE_DM(L, 4) MOE_DM(L, 6) MOE_DM(L, 8)
+    MOE_DML(64) MOE_DML(32) MOE_DML(16)
+#undef MOE_DML
+#undef MOE_DM
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 bool decode_shape_supported(const moe_config& c) {
@@ -333,9 +474,12 @@ static int staged_rows(const DecodeList& list, int K) {
     return std::max(1, std::min(most, (32 << 10) / (2 * K)));
 }
 
-hipError_t launch_ffn_decode(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
-                             const void* slot_base, const void* shared, const DecodeList& list, void* o, void* ws,
-                             hipStream_t s) {
+// o != null: gate/up, then down into the pair outputs o; else gate/up, then the fused
+// down + merge into out.
+static hipError_t launch_ffn_decode_impl(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
+                                         const void* slot_base, const void* shared, const DecodeList& list, void* o,
+                                         void* ws, hipStream_t s, const int32_t* ids, const float* w,
+                                         const uint32_t* mask, int32_t with_shared, const float* y_host, void* out) {
     const int gu_ch = ffn::chunks_per_row(c.w_dtype, c.hidden), d_ch = ffn::chunks_per_row(c.w_dtype, c.inter);
     int lpr, cpld;
     if (!pick_down(d_ch, &lpr, &cpld)) return hipErrorInvalidValue;
@@ -384,11 +528,52 @@ hipError_t launch_ffn_decode(const moe_config& c, const BlobLayout& lay, const v
     a.K = c.inter;
     a.nrows = c.hidden;
     a.nt = staged_rows(list, c.inter);
+    if (!o) {
+        a.m.ids = ids;
+        a.m.w = w;
+        a.m.y_host = y_host;
+        a.m.out = out;
+        for (int i = 0; i < kMaxExperts / 32; ++i) a.m.mask[i] = mask[i];
+        a.m.with_shared = with_shared;
+        switch (c.w_dtype) {
+            case MOE_W_F32: return launch_dm<WT_F32>(a, lpr, cpld, s);
+            case MOE_W_BF16: return launch_dm<WT_BF16>(a, lpr, cpld, s);
+            default: return launch_dm<WT_FP4>(a, lpr, cpld, s);
+        }
+    }
     switch (c.w_dtype) {
         case MOE_W_F32: return launch_d<WT_F32>(a, lpr, cpld, list.n, s);
         case MOE_W_BF16: return launch_d<WT_BF16>(a, lpr, cpld, list.n, s);
         default: return launch_d<WT_FP4>(a, lpr, cpld, list.n, s);
     }
+}
+
+hipError_t launch_ffn_decode_merge(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
+                                   const void* slot_base, const void* shared, const DecodeList& list,
+                                   const int32_t* ids, const float* w, const uint32_t* mask, int32_t with_shared,
+                                   const float* y_host, void* out, void* ws, hipStream_t s) {
+    // The fused kernel when every wave takes one entry and a workgroup covers at least 4
+    // output rows (at most 32 lanes per down row).  Measured on MI355X: with more entries a
+    // wave takes several experts one after another, and with 2 rows per workgroup (64 lanes
+    // per row) the per-workgroup merge outweighs the saved launch; both run slower fused
+    // than the separate down and merge kernels (pair outputs in the workspace).
+    int lpr = 64, cpl = 0;
+    pick_down(ffn::chunks_per_row(c.w_dtype, c.inter), &lpr, &cpl);
+    if (list.n <= kFusedWaves && c.top_k <= kFusedTopK && lpr <= 32)
+        return launch_ffn_decode_impl(c, lay, x, T, slot_base, shared, list, nullptr, ws, s, ids, w, mask,
+                                      with_shared, y_host, out);
+    void* o = static_cast<uint8_t*>(ws) + ws_layout(c, T).o;
+    hipError_t e = launch_ffn_decode_impl(c, lay, x, T, slot_base, shared, list, o, ws, s, nullptr, nullptr, nullptr,
+                                          0, nullptr, nullptr);
+    if (e != hipSuccess) return e;
+    return launch_merge(c, o, ids, w, mask, with_shared, y_host, T, out, s);
+}
+
+hipError_t launch_ffn_decode(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
+                             const void* slot_base, const void* shared, const DecodeList& list, void* o, void* ws,
+                             hipStream_t s) {
+    return launch_ffn_decode_impl(c, lay, x, T, slot_base, shared, list, o, ws, s, nullptr, nullptr, nullptr, 0,
+                                  nullptr, nullptr);
 }
 
 }  // namespace moe

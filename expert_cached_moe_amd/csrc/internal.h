@@ -42,7 +42,7 @@ inline int act_bytes(const moe_config& c) { return c.w_dtype == MOE_W_F32 ? 4 : 
 // The counter block sits at offset 0 (same address for every T): it must be zero
 // before the first call and every call leaves it zeroed.
 struct WsLayout {
-    int64_t ctr = 0, hist = 0, base = 0, tiles = 0, h = 0, bytes = 0;
+    int64_t ctr = 0, hist = 0, base = 0, tiles = 0, h = 0, o = 0, bytes = 0;
 };
 int64_t gemm_tile_ints(const moe_config& c, int32_t T);  // tile-list entries of the grouped GEMM
 constexpr int64_t kCtrBytes = 4 * (2 + kMaxExperts + 1 + 61);  // ticket, finished, per-entry counts
@@ -119,6 +119,12 @@ struct DecodeList {
 hipError_t launch_ffn_decode(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
                              const void* slot_base, const void* shared, const DecodeList& list, void* o, void* ws,
                              hipStream_t s);
+// Decode FFN with the gate-weighted merge fused into the down kernel: out = the result of
+// moe_merge_partial over the pair outputs launch_ffn_decode would write (bit-identical).
+hipError_t launch_ffn_decode_merge(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
+                                   const void* slot_base, const void* shared, const DecodeList& list,
+                                   const int32_t* ids, const float* w, const uint32_t* mask, int32_t with_shared,
+                                   const float* y_host, void* out, void* ws, hipStream_t s);
 bool decode_shape_supported(const moe_config& c);
 
 hipError_t launch_route(const moe_config& c, const float* logits, int32_t T, int32_t* ids, float* w,

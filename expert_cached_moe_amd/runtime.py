@@ -54,6 +54,13 @@ class LayerBuffers:
         B.moe_expert_ffn(self.ctx, x, T, h_ids, self.offsets, self.perm, slot_base, experts, slots, n, shared,
                          with_shared, self.o, self.ws, stream)
 
+    def ffn_merge(self, x, T, slot_base, experts, slots, h_ids, shared=None, with_shared=0, y_host=None, out=None,
+                  stream=None):
+        """Decode (T <= 8): the experts and the merge of their pair outputs in one call, from
+        this buffer set's last route (ids and gates) and the host copy h_ids of its ids."""
+        B.moe_expert_ffn_merge(self.ctx, x, T, h_ids, self.ids, self.w, slot_base, experts, slots, len(experts), shared,
+                               with_shared, y_host, out, self.ws, stream)
+
     def merge(self, gpu_experts, with_shared, y_host, T, out, stream=None):
         B.moe_merge_partial(self.ctx, self.o, self.ids, self.w, gpu_experts, len(gpu_experts), with_shared,
                             y_host, T, out, stream)

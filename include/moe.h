@@ -139,7 +139,8 @@ const char* moe_status_string(int status);
  * in the host pool and in the device slots, so a fill is one contiguous copy
  * ([B] "Elastic Memory": experts are read into their final host layout). */
 int64_t moe_expert_bytes(const moe_config* cfg);
-/* Device scratch bytes needed by moe_route + moe_expert_ffn for up to max_T tokens.
+/* Device scratch bytes needed by moe_route + moe_expert_ffn (+ moe_expert_ffn_merge) for
+ * up to max_T tokens.
  * The workspace must be zero-filled once before its first use; every call leaves
  * its first kilobytes (queue counters of the decode FFN) zeroed again, the rest is
  * scratch.  Calls that share a workspace must be ordered (one stream, or events). */
@@ -269,6 +270,24 @@ int moe_host_ffn(moe_ctx* ctx, const void* h_x, int32_t T, const int32_t* h_topk
 int moe_merge_partial(moe_ctx* ctx, const void* d_o, const int32_t* d_topk_ids, const float* d_topk_w,
                       const int32_t* h_gpu_experts, int32_t n_gpu, int32_t with_shared,
                       const float* d_y_host, int32_t T, void* d_out, hipStream_t s);
+
+/* Decode expert FFN and merge in one call (async on s): out as moe_merge_partial would
+ * write it from the pair outputs moe_expert_ffn would write for the same arguments
+ * (h_experts doubles as h_gpu_experts), bit for bit, without the pair outputs going
+ * through memory when the call lists at most 8 entries (routed experts + the shared
+ * one), k <= 8 and the decode kernel reads a down-projection row with at most 32 lanes
+ * (bf16 with I = 768 and MXFP4 with I = 1536 do; bf16 with I = 1536 does not): the down
+ * projection and the gate-weighted merge then share one kernel; otherwise the separate
+ * kernels run with the pair outputs in d_ws.
+ * Decode batches only: T <= 8, h_topk_ids given, and the shapes of the decode kernels
+ * (else MOE_ESHAPE); d_topk_ids / d_topk_w are moe_route's outputs for the same step
+ * (read on the device, so the call must follow moe_route on s).  Same buffers and
+ * errors as the two calls otherwise; d_y_host may be null.  ([B] "The q* Policy": the
+ * GPU experts' partial sum, merged exactly with the host part after the layer.) */
+int moe_expert_ffn_merge(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* h_topk_ids,
+                         const int32_t* d_topk_ids, const float* d_topk_w, const void* d_slot_base,
+                         const int32_t* h_experts, const int32_t* h_slots, int32_t n, const void* d_shared,
+                         int32_t with_shared, const float* d_y_host, void* d_out, void* d_ws, hipStream_t s);
 
 /* ---------------------------------------------------------------- layer streaming (prefill) */
 /* One T-token prefill chunk through cfg.n_layers MoE layers whose expert pools

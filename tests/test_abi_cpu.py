@@ -308,3 +308,32 @@ def test_pack_rejects_nan_scale():
     with pytest.raises(B.MoeError):
         B.moe_pack_expert(cfg, w["wg"], w["wu"], w["wd"], sg, w["su"], w["sd"], blob)
     assert (blob == 7).all()                    # no side effect on error
+
+
+def test_ffn_merge_argument_errors():
+    """moe_expert_ffn_merge rejects what it cannot run before touching the GPU: batches
+    above the decode size, a missing host copy of the ids, bad or repeated expert ids,
+    a shared expert the config does not have.  (The addresses are never dereferenced.)"""
+    wl = synth.workload("a3b_decode_bf16")
+    cfg = config(wl)
+    ctx = B.moe_create(cfg)
+    ids = np.arange(wl.k, dtype=np.int32)[None, :]
+    ex = np.arange(wl.k, dtype=np.int32)
+    good = dict(d_x=64, T=1, h_topk_ids=ids, d_topk_ids=64, d_topk_w=64, d_slot_base=64, h_experts=ex,
+                h_slots=ex, n=wl.k, d_shared=None, with_shared=0, d_y_host=None, d_out=64, d_ws=64)
+
+    def status(**kw):
+        args = dict(good, **kw)
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_expert_ffn_merge(ctx, **args)
+        return ei.value.status
+
+    assert status(T=9, h_topk_ids=np.zeros((9, wl.k), np.int32)) == B.MOE_ESHAPE
+    assert status(h_topk_ids=None) == B.MOE_EINVAL
+    assert status(d_topk_w=None) == B.MOE_EINVAL
+    assert status(h_experts=np.array([0, 1, 2, 3, 4, 5, 6, wl.E], np.int32)) == B.MOE_EINVAL
+    assert status(h_experts=np.array([0, 1, 2, 3, 4, 5, 6, 6], np.int32)) == B.MOE_EINVAL
+    assert status(h_topk_ids=np.array([[0, 1, 2, 3, 4, 5, 6, -1]], np.int32)) == B.MOE_EINVAL
+    assert status(h_topk_ids=np.array([[0, 1, 2, 3, 4, 5, 6, 6]], np.int32)) == B.MOE_EINVAL
+    assert status(with_shared=1, d_shared=64) == B.MOE_EINVAL
+    B.moe_destroy(ctx)

@@ -178,6 +178,20 @@ def _decode_case(B, name, T, frac, seed, host_ids=True, wl=None):
     # bitwise run-to-run determinism
     out2 = G.run(logits, x, gpu, ws, host_ids=host_ids)
     assert torch.equal(out, out2)
+    if host_ids:
+        # experts and merge in one call (moe_expert_ffn_merge) against the two calls, bit for
+        # bit, with a host part when some experts are on the host
+        yh = torch.from_numpy(np.random.default_rng(seed + 7).standard_normal(T * wl.H).astype(np.float32)).cuda() \
+            if frac < 1 else None
+        slots = [G.slot[e] for e in gpu]
+        h_ids = G.L.ids[: T * wl.k].cpu().numpy().reshape(T, wl.k)
+        dx = _dev_act(x)
+        two, one = torch.empty_like(out), torch.full_like(out, 7)
+        G.L.ffn(dx, T, G.pool, gpu, slots, G.shared, ws, h_ids=h_ids)
+        G.L.merge(gpu, ws, yh, T, two)
+        G.L.ffn_merge(dx, T, G.pool, gpu, slots, h_ids, G.shared, ws, yh, one)
+        torch.cuda.synchronize()
+        assert torch.equal(one, two), (name, T, frac)
     G.L.close()
     return err.max()
 
