@@ -8,9 +8,9 @@
 //
 // Selection order: logit descending, lower expert id on equal logits (-0 == +0).
 // Gates: softmax renormalised over the k selected logits (or over all experts).
-// Selection: k rounds of a wave-wide maximum over 64-bit keys that pack an
-// order-preserving key of the logit with the inverted expert id, so the order is
-// one integer compare and every lane ends each round holding the winner.
+// Selection: k rounds of a wave-wide maximum over an order-preserving 32-bit key of
+// the logit; ballots over the lanes holding that key then name the lowest expert id,
+// whose key is cleared for the next round.
 // Grouping: stable counting sort of pairs p = t*k + j by expert (ascending p
 // within an expert), with its inverse.  Integer work is exact and deterministic:
 // counts use integer LDS atomics, ranks use wave ballots.
@@ -38,73 +38,70 @@ __device__ __forceinline__ float key_value(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// (logit key, inverted id) as one 64-bit key, split in halves: a larger key ranks first
-// (larger logit, then lower id).  0 marks an expert that is out of the running.
-struct Key64 {
-    uint32_t hi, lo;
-};
-__device__ __forceinline__ bool key_gt(Key64 a, Key64 b) { return a.hi > b.hi || (a.hi == b.hi && a.lo > b.lo); }
-__device__ __forceinline__ void key_max(Key64& a, Key64 b) {
-    const bool g = key_gt(b, a);
-    a.hi = g ? b.hi : a.hi;
-    a.lo = g ? b.lo : a.lo;
-}
+// Wave-wide maximum of an unsigned key, left in every lane: butterflies inside each row of
+// 16 lanes (DPP quad swaps, rotations by 4 and 8), then row pairs and wave halves exchanged
+// with permlane16_swap / permlane32_swap.
 template <int CTRL>
-__device__ __forceinline__ void key_dpp_max(Key64& a) {
-    Key64 b;
-    b.hi = uint32_t(__builtin_amdgcn_mov_dpp(int(a.hi), CTRL, 0xF, 0xF, false));
-    b.lo = uint32_t(__builtin_amdgcn_mov_dpp(int(a.lo), CTRL, 0xF, 0xF, false));
-    key_max(a, b);
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t a) {
+    return max(a, uint32_t(__builtin_amdgcn_mov_dpp(int(a), CTRL, 0xF, 0xF, false)));
 }
-
-// Wave-wide maximum of a key, left in every lane: butterflies inside each row of 16 lanes
-// (DPP quad swaps, rotations by 4 and 8), then row pairs and wave halves exchanged with
-// permlane16_swap / permlane32_swap.
-__device__ __forceinline__ Key64 wave_max(Key64 a) {
-    key_dpp_max<0xB1>(a);   // quad_perm [1,0,3,2]
-    key_dpp_max<0x4E>(a);   // quad_perm [2,3,0,1]
-    key_dpp_max<0x124>(a);  // row_ror:4
-    key_dpp_max<0x128>(a);  // row_ror:8
-    const auto h16 = __builtin_amdgcn_permlane16_swap(a.hi, a.hi, false, false);
-    const auto l16 = __builtin_amdgcn_permlane16_swap(a.lo, a.lo, false, false);
-    a = Key64{h16[0], l16[0]};
-    key_max(a, Key64{h16[1], l16[1]});
-    const auto h32 = __builtin_amdgcn_permlane32_swap(a.hi, a.hi, false, false);
-    const auto l32 = __builtin_amdgcn_permlane32_swap(a.lo, a.lo, false, false);
-    a = Key64{h32[0], l32[0]};
-    key_max(a, Key64{h32[1], l32[1]});
-    return a;
+__device__ __forceinline__ uint32_t wave_umax(uint32_t a) {
+    a = dpp_umax<0xB1>(a);   // quad_perm [1,0,3,2]
+    a = dpp_umax<0x4E>(a);   // quad_perm [2,3,0,1]
+    a = dpp_umax<0x124>(a);  // row_ror:4
+    a = dpp_umax<0x128>(a);  // row_ror:8
+    const auto h16 = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+    a = max(h16[0], h16[1]);
+    const auto h32 = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+    return max(h32[0], h32[1]);
 }
 
 // Route one token with one wave.  EPL = experts per lane (ceil(E/64)); lane l holds experts
-// l + 64 i.  k rounds of a wave-wide maximum over the packed keys; lane j keeps the j-th pick.
+// l + 64 i.  k rounds: the wave-wide maximum of the logit keys, then the lowest expert id
+// holding it (ballots per slot i, lowest slot first, then lowest lane, since the id is
+// l + 64 i), whose key is cleared to 0; lane j keeps the j-th pick.  Keys of finite logits
+// are nonzero, so 0 marks an expert out of the running.
 template <int EPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ lrow, int E, int k, int renorm,
                                             int32_t* __restrict__ ids_out, float* __restrict__ w_out,
                                             int32_t* __restrict__ lds_ids) {
     const int lane = dev::lane_id();
     float v[EPL];
-    Key64 key[EPL];
+    uint32_t key[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + kWave * i;
         const bool live = e < E;
         v[i] = live ? lrow[e] : 0.0f;
-        key[i] = live ? Key64{order_key(v[i]), ~uint32_t(e)} : Key64{0u, 0u};
+        key[i] = live ? order_key(v[i]) : 0u;
     }
-    Key64 mine{0u, 0u};
+    uint32_t mine = 0u;
+    int my_e = 0;
     for (int j = 0; j < k; ++j) {
-        Key64 best = key[0];
+        uint32_t best = key[0];
 #pragma unroll
-        for (int i = 1; i < EPL; ++i) key_max(best, key[i]);
-        best = wave_max(best);
+        for (int i = 1; i < EPL; ++i) best = max(best, key[i]);
+        best = wave_umax(best);
+        uint64_t hit = 0;
+        int slot = 0;
+#pragma unroll
+        for (int i = EPL - 1; i >= 0; --i) {
+            const uint64_t b = __ballot(key[i] == best);
+            if (b) {
+                hit = b;
+                slot = i;
+            }
+        }
+        const int wl = __builtin_ctzll(hit);
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
-            if (key[i].hi == best.hi && key[i].lo == best.lo) key[i] = Key64{0u, 0u};
-        if (lane == j) mine = best;
+            if (i == slot && lane == wl) key[i] = 0u;
+        if (lane == j) {
+            mine = best;
+            my_e = wl + kWave * slot;
+        }
     }
-    const float my_v = key_value(mine.hi);
-    const int my_e = int(~mine.lo);
+    const float my_v = key_value(mine);
     const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
     // softmax over the selected logits (or over all E), shifted by the largest logit
     const float ex = lane < k ? expf(my_v - v0) : 0.0f;
@@ -128,7 +125,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lrow, int 
 }
 
 template <int EPL>
-__device__ void route_tokens(const float* __restrict__ logits, int T, int E, int k, int renorm, int t0,
+__device__ __forceinline__ void route_tokens(const float* __restrict__ logits, int T, int E, int k, int renorm, int t0,
                              int tstride, int32_t* __restrict__ ids, float* __restrict__ w,
                              int32_t* __restrict__ lds_ids) {
     const int wave = threadIdx.x / kWave;
@@ -137,7 +134,7 @@ __device__ void route_tokens(const float* __restrict__ logits, int T, int E, int
                          lds_ids ? lds_ids + int64_t(t) * k : nullptr);
 }
 
-__device__ void route_dispatch(const float* logits, int T, int E, int k, int renorm, int t0, int tstride,
+__device__ __forceinline__ void route_dispatch(const float* logits, int T, int E, int k, int renorm, int t0, int tstride,
                                int32_t* ids, float* w, int32_t* lds_ids) {
     const int epl = (E + kWave - 1) / kWave;
     switch (epl) {
