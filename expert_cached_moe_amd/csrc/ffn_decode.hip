@@ -89,6 +89,34 @@ __device__ __forceinline__ void read_staged(ActChunk<WT_FP4>& av, const uint4* x
     for (int i = 0; i < 4; ++i) av.v[i] = xs[slot * units + i * cpr + chunk];
 }
 
+// MXFP4 block scales of consecutive weight rows.  The scale bytes of rows [r0, r0 + n) are
+// contiguous (K/32 bytes a row); lane l loads dword l of every 64-dword piece of that run, and
+// a lane that needs byte b of the run takes it from the lane holding dword b/4 (ds_bpermute).
+// One dword load a lane per piece replaces one byte load per weight chunk: a vector memory
+// instruction costs the address pipeline about the same whatever it moves, and byte loads of
+// 64 bytes a wave made the MXFP4 decode kernels 7-8% slower (measured on MI355X).
+template <int ND>
+struct ScaleRun {
+    uint32_t d[ND];
+    // run: the run's first scale byte; ndw: dwords readable from it
+    __device__ __forceinline__ void load(const uint8_t* run, int ndw, int lane) {
+#pragma unroll
+        for (int k = 0; k < ND; ++k) {
+            const int i = 64 * k + lane;
+            d[k] = *reinterpret_cast<const uint32_t*>(run + 4 * (i < ndw ? i : 0));
+        }
+    }
+    // byte b of the run, from piece k = b / 256 (the same in every lane of the call)
+    __device__ __forceinline__ uint8_t byte(int k, int b) const {
+        const int v = __builtin_amdgcn_ds_bpermute(b & 252, int(d[k]));
+        return uint8_t(uint32_t(v) >> (8 * (b & 3)));
+    }
+};
+
+// Keeps the loads issued above it ahead of the code below it (the scale permutes below wait
+// for the scale loads, which were issued first, and must not hold back the weight loads).
+__device__ __forceinline__ void loads_issued() { asm volatile("" ::: "memory"); }
+
 // Pair row and activation row of the i-th set bit of the expert's token mask.
 struct TokenIter {
     uint32_t mask, jpack;
@@ -132,17 +160,29 @@ __global__ void __launch_bounds__(64 * kGateUpWaves) k_decode_gate_up(const Deco
         const int i = col0 + (q < HALF ? q : q - HALF);
         return (i / 16) * 32 + (i % 16) + (q < HALF ? 0 : 16);
     };
+    // MXFP4: the scales of the gate rows and of the up rows (HALF consecutive rows each)
+    constexpr int NDW = HALF * 16 * CPL, ND = (NDW + 63) / 64;
+    ScaleRun<ND> sr[2];
+    if constexpr (WT == WT_FP4) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) sr[h].load(blob + a.off_s + int64_t(row_of(h * HALF)) * (a.H / 32), NDW, lane);
+    }
     uint4 wv[RPW][CPL];
     uint8_t sv[RPW][CPL];
 #pragma unroll
     for (int q = 0; q < RPW; ++q) {
         const int64_t r = row_of(q);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            wv[q][c] = load_w(blob + a.off_w + r * row_bytes, c * kWave + lane);
-            sv[q][c] = WT == WT_FP4 ? blob[a.off_s + r * (a.H / 32) + c * kWave + lane] : uint8_t(0);
-        }
+        for (int c = 0; c < CPL; ++c) wv[q][c] = load_w(blob + a.off_w + r * row_bytes, c * kWave + lane);
     }
+    if constexpr (WT == WT_FP4) loads_issued();
+#pragma unroll
+    for (int q = 0; q < RPW; ++q)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int base = (q % HALF) * 64 * CPL + c * kWave;   // run byte of chunk c * 64 of row q
+            sv[q][c] = WT == WT_FP4 ? sr[q / HALF].byte(base / 256, base + lane) : uint8_t(0);
+        }
     // one token: dot products of the wave's rows with x[t], SwiGLU, store h[p]
     auto token = [&](int p, auto&& act_chunk) {
 #pragma unroll
@@ -173,22 +213,29 @@ __global__ void __launch_bounds__(64 * kGateUpWaves) k_decode_gate_up(const Deco
             });
     } else {
         // groups of up to nt token rows of x, staged after the weight loads are issued; every
-        // wave takes the same token sequence, so the barriers are uniform
+        // wave takes the same token sequence, so the barriers are uniform.  The first group's
+        // copies are issued ahead of the loop: at the loop's entry the compiler waits for the
+        // weight loads (register copies), which would otherwise put the activation fetch
+        // behind the whole weight stream.
         extern __shared__ __attribute__((aligned(16))) uint4 xs[];
-        bool have = it.next(p, t);
-        while (have) {
-            TokenIter g = it;
-            int gp = p, gt = t, n = 0;
+        auto stage_group = [&](TokenIter g, int gp, int gt) {
+            int n = 0;
             for (bool gh = true; n < a.nt && gh; ++n) {
                 stage_row(xs, a.act, gt, a.H, n, wave, WPB, lane);
                 gh = g.next(gp, gt);
             }
+            return n;
+        };
+        bool have = it.next(p, t);
+        int n = have ? stage_group(it, p, t) : 0;
+        while (have) {
             barrier_loads();
             for (int s = 0; s < n; ++s) {
                 token(p, [&](ActChunk<WT>& av, int c) { read_staged(av, xs, a.H, s, c * kWave + lane); });
                 have = it.next(p, t);
             }
             __syncthreads();            // group read before the next one lands
+            if (have) n = stage_group(it, p, t);
         }
     }
 }
@@ -222,17 +269,41 @@ __global__ void __launch_bounds__(64 * kDownWaves) k_decode_down(const DecodeArg
 #pragma unroll
         for (int c = 0; c < CPL; ++c) load_act<WT>(av0[c], a.act + (int64_t(p) * a.I + int64_t(c * LPR + lr) * EPC) * AB);
     }
+    // MXFP4 with at most 4 chunks a lane: the scales of each pass's RPP rows (64 * CPL bytes) as
+    // one run, clipped at the matrix end; wider rows load a scale byte per chunk
+    constexpr bool kRun = WT == WT_FP4 && 16 * CPL <= 64;
+    ScaleRun<1> sr[NPASS];
+    if constexpr (kRun) {
+#pragma unroll
+        for (int q = 0; q < NPASS; ++q) {
+            const int rs = row0 + q * RPP;
+            const int avail = rs < a.nrows ? min(16 * CPL, (a.nrows - rs) * (a.I / 128)) : 0;
+            sr[q].load(blob + a.off_s + (avail ? int64_t(rs) * (a.I / 32) : 0), avail ? avail : 1, lane);
+        }
+    }
     uint4 wv[NPASS][CPL];
     uint8_t sv[NPASS][CPL];
 #pragma unroll
     for (int q = 0; q < NPASS; ++q) {
         const int r = row0 + q * RPP + g;
         const bool ok = r < a.nrows;
+        const int rl = ok ? r : a.nrows - 1;     // unconditional loads (a loaded register copied inside
+                                                 // a branch waits for every load): rows past the end
+                                                 // reread the last row, and are not stored
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            wv[q][c] = ok ? load_w(blob + a.off_w + int64_t(r) * row_bytes, c * LPR + lr) : make_uint4(0, 0, 0, 0);
-            sv[q][c] = (WT == WT_FP4 && ok) ? blob[a.off_s + int64_t(r) * (a.I / 32) + c * LPR + lr] : uint8_t(127);
+            wv[q][c] = load_w(blob + a.off_w + int64_t(rl) * row_bytes, c * LPR + lr);
+            if constexpr (!kRun)
+                sv[q][c] = (WT == WT_FP4 && ok) ? blob[a.off_s + int64_t(r) * (a.I / 32) + c * LPR + lr] : uint8_t(127);
         }
+    }
+    if constexpr (kRun) {
+        loads_issued();
+#pragma unroll
+        for (int q = 0; q < NPASS; ++q)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                sv[q][c] = row0 + q * RPP + g < a.nrows ? sr[q].byte(0, g * LPR * CPL + c * LPR + lr) : uint8_t(127);
     }
     // one pair row: dot products of the wave's rows with h[p], store o[p]
     auto token = [&](int p, auto&& act_chunk) {
@@ -262,28 +333,33 @@ __global__ void __launch_bounds__(64 * kDownWaves) k_decode_down(const DecodeArg
                 load_act<WT>(av, a.act + (int64_t(p) * a.I + int64_t(c * LPR + lr) * EPC) * AB);
             });
     } else {
-        // groups of up to nt pair rows of h (uniform over the workgroup, as above)
+        // groups of up to nt pair rows of h (uniform over the workgroup; the first group's
+        // copies issued ahead of the loop, as above)
         extern __shared__ __attribute__((aligned(16))) uint4 xs[];
-        while (have) {
-            TokenIter gi = it;
-            int gp = p, gt = t, n = 0;
+        auto stage_group = [&](TokenIter g, int gp, int gt) {
+            int n = 0;
             for (bool gh = true; n < a.nt && gh; ++n) {
                 stage_row(xs, a.act, gp, a.I, n, wave, kDownWaves, lane);
-                gh = gi.next(gp, gt);
+                gh = g.next(gp, gt);
             }
+            return n;
+        };
+        int n = have ? stage_group(it, p, t) : 0;
+        while (have) {
             barrier_loads();
             for (int s = 0; s < n; ++s) {
                 token(p, [&](ActChunk<WT>& av, int c) { read_staged(av, xs, a.I, s, c * LPR + lr); });
                 have = it.next(p, t);
             }
             __syncthreads();            // group read before the next one lands
+            if (have) n = stage_group(it, p, t);
         }
     }
 }
 
 // Down projection and gate-weighted merge in one launch.  A workgroup owns RPW rows of the
-// output for every listed expert: wave w computes the pair outputs of entries w, w + 8, ...
-// for those rows exactly as k_decode_down does (same lanes, chunks and reduction order),
+// output for every listed expert: wave w computes the pair outputs of entry w for those rows
+// exactly as k_decode_down does (same lanes, chunks and reduction order),
 // rounds them to the activation dtype and keeps them in LDS; after one barrier each
 // (token, row) is merged exactly as k_merge does: gate-weighted pair outputs of the GPU
 // experts in order j = 0..k-1 (fmaf), then the shared expert's row, then the host part.
@@ -301,7 +377,9 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_decode_down_merge(const De
     constexpr int RPW = NPASS * RPP;
     static_assert(NPASS <= LPR && RPW <= 8, "pass layout");
     __shared__ float s_o[(kDecodeMaxT * kFusedTopK + kDecodeMaxT) * RPW];
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    // wave index made uniform, so the list reads (ent, tokmask, jpack at [ei]) are scalar loads:
+    // as vector loads their waits also waited for the merge inputs issued ahead of them
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int g = lane / LPR, lr = lane % LPR;
     const int64_t row_bytes = Fmt<WT>::row_bytes(a.I);
     const int row0 = blockIdx.x * RPW;
@@ -320,7 +398,11 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_decode_down_merge(const De
     }
     float myh = 0.0f;
     if (a.m.y_host) myh = a.m.y_host[int64_t(mt) * a.H + (mrow < a.H ? mrow : 0)];
-    for (int ei = wave; ei < a.list.n; ei += kFusedWaves) {
+    // one entry per wave (the host launches this kernel for lists of at most kFusedWaves
+    // entries); no loop over entries, whose back edge would make the compiler wait for the
+    // merge inputs before the weight loads (register reuse across iterations)
+    if (wave < a.list.n) {
+        const int ei = wave;
         const int entry = a.list.ent[ei];
         const bool shared = (entry & 1023) == kSharedTag;
         const uint8_t* blob = shared ? a.shared_blob : a.slot_base + int64_t(entry >> 10) * a.blob_bytes;
@@ -334,17 +416,41 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_decode_down_merge(const De
             for (int c = 0; c < CPL; ++c)
                 load_act<WT>(av0[c], a.act + (int64_t(p) * a.I + int64_t(c * LPR + lr) * EPC) * AB);
         }
+        // MXFP4 with at most 4 chunks a lane: the scales of each pass's RPP rows (64 * CPL bytes) as
+        // one run, clipped at the matrix end; wider rows load a scale byte per chunk
+        constexpr bool kRun = WT == WT_FP4 && 16 * CPL <= 64;
+        ScaleRun<1> sr[NPASS];
+        if constexpr (kRun) {
+#pragma unroll
+            for (int q = 0; q < NPASS; ++q) {
+                const int rs = row0 + q * RPP;
+                const int avail = rs < a.nrows ? min(16 * CPL, (a.nrows - rs) * (a.I / 128)) : 0;
+                sr[q].load(blob + a.off_s + (avail ? int64_t(rs) * (a.I / 32) : 0), avail ? avail : 1, lane);
+            }
+        }
         uint4 wv[NPASS][CPL];
         uint8_t sv[NPASS][CPL];
 #pragma unroll
         for (int q = 0; q < NPASS; ++q) {
             const int r = row0 + q * RPP + g;
             const bool ok = r < a.nrows;
+            const int rl = ok ? r : a.nrows - 1;     // unconditional loads (a loaded register copied inside
+                                                     // a branch waits for every load): rows past the end
+                                                     // reread the last row, and are not stored
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                wv[q][c] = ok ? load_w(blob + a.off_w + int64_t(r) * row_bytes, c * LPR + lr) : make_uint4(0, 0, 0, 0);
-                sv[q][c] = (WT == WT_FP4 && ok) ? blob[a.off_s + int64_t(r) * (a.I / 32) + c * LPR + lr] : uint8_t(127);
+                wv[q][c] = load_w(blob + a.off_w + int64_t(rl) * row_bytes, c * LPR + lr);
+                if constexpr (!kRun)
+                    sv[q][c] = (WT == WT_FP4 && ok) ? blob[a.off_s + int64_t(r) * (a.I / 32) + c * LPR + lr] : uint8_t(127);
             }
+        }
+        if constexpr (kRun) {
+            loads_issued();
+#pragma unroll
+            for (int q = 0; q < NPASS; ++q)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    sv[q][c] = row0 + q * RPP + g < a.nrows ? sr[q].byte(0, g * LPR * CPL + c * LPR + lr) : uint8_t(127);
         }
         auto token = [&](int p, auto&& act_chunk) {
 #pragma unroll
