@@ -95,11 +95,11 @@ def payload_bytes(wl):
 # fetch counts are scaled by 262144 / 131080 and write counts by 1.  A record applies only
 # while the decode kernel sources hash to the value it was taken with.
 DECODE_SOURCES = ("ffn_decode.hip", "ffn_common.h", "device_common.h")
-_SRC = "b435705808ac4f596f00a27207fbb0a9ab5c24d234df3292344e4f5a5409ab81"
+_SRC = "390e133392962c096128c8d72ea310da36137216896f18e8f8b8e49e58f1c0c3"
 TRAFFIC = {
-    ("a3b_decode_bf16", 1): {"sha256": _SRC, "fetch_kib": 24613.0 + 12362.5, "write_kib": 48.0 + 32.0},
+    ("a3b_decode_bf16", 1): {"sha256": _SRC, "fetch_kib": 24613.0 + 12356.5, "write_kib": 48.0 + 32.0},
     ("v4flash_decode_bf16", 1): {"sha256": _SRC, "fetch_kib": 86072.0 + 43114.5, "write_kib": 84.0 + 56.0},
-    ("v4flash_mxfp4", 1): {"sha256": _SRC, "fetch_kib": 22921.5 + 11542.5, "write_kib": 42.0 + 56.0},
+    ("v4flash_mxfp4", 1): {"sha256": _SRC, "fetch_kib": 22922.5 + 11552.0, "write_kib": 42.0 + 56.0},
 }
 FETCH_FACTOR = 262144.0 / 131080.0
 WRITE_FACTOR = 1.0
