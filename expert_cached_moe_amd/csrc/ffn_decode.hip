@@ -384,20 +384,25 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_decode_down_merge(const De
     const int64_t row_bytes = Fmt<WT>::row_bytes(a.I);
     const int row0 = blockIdx.x * RPW;
     // the merge's ids, gates and host part, issued first so their latency hides under the
-    // weight stream (thread i < T*RPW merges token i / RPW, row i % RPW; the loads are
-    // unconditional, at index 0 for the other threads, so none waits behind a branch)
+    // weight stream.  Thread i < T*RPW (all in wave 0) merges token i / RPW, row i % RPW; only
+    // wave 0 loads them (17 loads a wave in every wave would crowd the weight loads in the
+    // address path), inside wave 0 unconditionally (index 0 for the other threads; the host
+    // part through a valid stand-in address), so no load waits behind a branch
     const bool merger = tid < a.T * RPW;
     const int mt = merger ? tid / RPW : 0, mrl = tid % RPW, mrow = row0 + mrl;
     int mid[kFusedTopK];
     float mw[kFusedTopK];
+    float myh;
+    if (wave == 0) {
 #pragma unroll
-    for (int j = 0; j < kFusedTopK; ++j) {
-        const int pj = merger && j < a.k ? mt * a.k + j : 0;
-        mid[j] = a.m.ids[pj];
-        mw[j] = a.m.w[pj];
+        for (int j = 0; j < kFusedTopK; ++j) {
+            const int pj = merger && j < a.k ? mt * a.k + j : 0;
+            mid[j] = a.m.ids[pj];
+            mw[j] = a.m.w[pj];
+        }
+        const float* yh = a.m.y_host ? a.m.y_host + int64_t(mt) * a.H + (mrow < a.H ? mrow : 0) : a.m.w;
+        myh = *yh;
     }
-    float myh = 0.0f;
-    if (a.m.y_host) myh = a.m.y_host[int64_t(mt) * a.H + (mrow < a.H ? mrow : 0)];
     // one entry per wave (the host launches this kernel for lists of at most kFusedWaves
     // entries); no loop over entries, whose back edge would make the compiler wait for the
     // merge inputs before the weight loads (register reuse across iterations)
@@ -483,7 +488,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_decode_down_merge(const De
             });
     }
     __syncthreads();
-    if (merger && mrow < a.H) {
+    if (wave == 0 && merger && mrow < a.H) {
         float acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < kFusedTopK; ++j) {
@@ -493,7 +498,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_decode_down_merge(const De
         }
         const float sh = a.m.with_shared ? s_o[(a.T * a.k + mt) * RPW + mrl] : 0.0f;
         acc += sh;
-        acc += myh;
+        acc += a.m.y_host ? myh : 0.0f;
         if (WT == WT_F32)
             static_cast<float*>(a.m.out)[int64_t(mt) * a.H + mrow] = acc;
         else

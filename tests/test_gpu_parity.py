@@ -206,12 +206,14 @@ def test_decode_ffn_merge_parity(B, name, T, frac):
 
 
 @pytest.mark.parametrize("wdtype,H,I,T", [("f32", 512, 256, 1), ("f32", 512, 256, 5), ("bf16", 1024, 512, 1),
-                                          ("bf16", 1024, 512, 8), ("mxfp4", 2048, 1024, 1), ("mxfp4", 8192, 512, 8)])
+                                          ("bf16", 1024, 512, 8), ("mxfp4", 2048, 1024, 1), ("mxfp4", 8192, 512, 8),
+                                          ("mxfp4", 16384, 512, 2)])
 def test_decode_other_shapes(B, wdtype, H, I, T):
     """Decode at hidden/intermediate sizes other than the workloads' (16 experts, top-4):
     the kernels pick their lanes-per-row and chunks-per-lane from the shape.  MXFP4 at
     hidden 8192 stages two token rows of x per group in LDS, so the shared expert's 8
-    tokens take four groups."""
+    tokens take four groups; at hidden 16384 a gate/up lane holds 8 chunks, so the block
+    scales of its rows span two 64-dword pieces, and one token row fills the staging LDS."""
     print(f"[decode-other-shapes] {wdtype} H={H} I={I} T={T}", flush=True)
     import dataclasses
     base = synth.workload({"f32": "tiny_fp32", "bf16": "a3b_decode_bf16", "mxfp4": "v4flash_mxfp4"}[wdtype])
