@@ -24,35 +24,52 @@ struct MergeArgs {
     uint32_t mask[kMaxExperts / 32];
 };
 
-// Four consecutive values of a pair-output row, raw (16 bytes of fp32 or 8 of bf16); they are
-// loaded first and widened after every load of the thread is in flight.
-template <bool BF16> struct Raw4;
-template <> struct Raw4<true> { typedef uint2 T; };
-template <> struct Raw4<false> { typedef float4 T; };
+// N consecutive values of a pair-output row per thread, raw: 8 bf16 (16 bytes) or 4 fp32 (16
+// bytes), so every load instruction of a wave moves 1 KiB.  They are loaded first and widened
+// after every load of the thread is in flight.
+template <bool BF16> struct Piece;
+template <> struct Piece<true> {
+    typedef uint4 T;
+    static constexpr int N = 8;
+};
+template <> struct Piece<false> {
+    typedef float4 T;
+    static constexpr int N = 4;
+};
 
 template <bool BF16>
-__device__ __forceinline__ typename Raw4<BF16>::T load_raw4(const void* o, int64_t idx) {
-    if constexpr (BF16) return *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(o) + idx);
+__device__ __forceinline__ typename Piece<BF16>::T load_piece(const void* o, int64_t idx) {
+    if constexpr (BF16) return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(o) + idx);
     else return *reinterpret_cast<const float4*>(static_cast<const float*>(o) + idx);
 }
 
-__device__ __forceinline__ float4 widen(uint2 r) {
-    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u), __uint_as_float(r.y << 16),
-                       __uint_as_float(r.y & 0xFFFF0000u));
+__device__ __forceinline__ void widen(uint4 r, float (&f)[8]) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
 }
-__device__ __forceinline__ float4 widen(float4 r) { return r; }
+__device__ __forceinline__ void widen(float4 r, float (&f)[4]) {
+    f[0] = r.x;
+    f[1] = r.y;
+    f[2] = r.z;
+    f[3] = r.w;
+}
 
 template <bool BF16>
 __global__ void __launch_bounds__(256) k_merge(const MergeArgs a) {
+    constexpr int N = Piece<BF16>::N;
+    typedef typename Piece<BF16>::T Raw;
     const int t = blockIdx.y;
-    const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const int c = (blockIdx.x * 256 + threadIdx.x) * N;
     if (c >= a.H) return;
     // every partial row of the token is loaded at once (rows of CPU experts hold stale
     // values and are dropped by a select, never multiplied), next to the ids and gates
-    typename Raw4<BF16>::T v[kMaxTopK];
+    Raw v[kMaxTopK];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
-        v[j] = (a.o && j < a.k) ? load_raw4<BF16>(a.o, (int64_t(t) * a.k + j) * a.H + c) : typename Raw4<BF16>::T{};
+    for (int j = 0; j < kMaxTopK; ++j) v[j] = (a.o && j < a.k) ? load_piece<BF16>(a.o, (int64_t(t) * a.k + j) * a.H + c) : Raw{};
     float g[kMaxTopK];
     int64_t row[kMaxTopK];
     // the mask words are read up front and picked by compare, so the only memory access
@@ -76,29 +93,50 @@ __global__ void __launch_bounds__(256) k_merge(const MergeArgs a) {
             }
         }
     }
-    float4 sh = make_float4(0.f, 0.f, 0.f, 0.f), yh = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (a.with_shared) sh = widen(load_raw4<BF16>(a.o, (int64_t(a.T) * a.k + t) * a.H + c));
-    if (a.y_host) yh = *reinterpret_cast<const float4*>(a.y_host + int64_t(t) * a.H + c);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    Raw shr{};
+    if (a.with_shared) shr = load_piece<BF16>(a.o, (int64_t(a.T) * a.k + t) * a.H + c);
+    float yh[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) yh[i] = 0.0f;
+    if (a.y_host) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const float4 q = *reinterpret_cast<const float4*>(a.y_host + int64_t(t) * a.H + c + i);
+            yh[i] = q.x;
+            yh[i + 1] = q.y;
+            yh[i + 2] = q.z;
+            yh[i + 3] = q.w;
+        }
+    }
+    float acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = 0.0f;
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
         if (row[j] >= 0) {
-            const float4 f = widen(v[j]);
-            acc.x = fmaf(g[j], f.x, acc.x);
-            acc.y = fmaf(g[j], f.y, acc.y);
-            acc.z = fmaf(g[j], f.z, acc.z);
-            acc.w = fmaf(g[j], f.w, acc.w);
+            float f[N];
+            widen(v[j], f);
+#pragma unroll
+            for (int i = 0; i < N; ++i) acc[i] = fmaf(g[j], f[i], acc[i]);
         }
     }
-    acc.x += sh.x; acc.y += sh.y; acc.z += sh.z; acc.w += sh.w;
-    acc.x += yh.x; acc.y += yh.y; acc.z += yh.z; acc.w += yh.w;
-    if (BF16) {
-        uint2 r;
-        r.x = dev::pack_bf16x2(acc.x, acc.y);
-        r.y = dev::pack_bf16x2(acc.z, acc.w);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + int64_t(t) * a.H + c) = r;
+    float sh[N];
+    widen(shr, sh);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        acc[i] += sh[i];
+        acc[i] += yh[i];
+    }
+    if constexpr (BF16) {
+        uint4 r;
+        r.x = dev::pack_bf16x2(acc[0], acc[1]);
+        r.y = dev::pack_bf16x2(acc[2], acc[3]);
+        r.z = dev::pack_bf16x2(acc[4], acc[5]);
+        r.w = dev::pack_bf16x2(acc[6], acc[7]);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + int64_t(t) * a.H + c) = r;
     } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + int64_t(t) * a.H + c) = acc;
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + int64_t(t) * a.H + c) =
+            make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
 }
 
@@ -119,7 +157,8 @@ hipError_t launch_merge(const moe_config& c, const void* o, const int32_t* ids, 
     a.with_shared = with_shared;
     a.out_bf16 = c.w_dtype != MOE_W_F32;
     for (int i = 0; i < kMaxExperts / 32; ++i) a.mask[i] = gpu_mask[i];
-    const dim3 grid((c.hidden / 4 + 255) / 256, T);
+    const int per_thread = a.out_bf16 ? 8 : 4;           // values per thread (16 bytes of pair output)
+    const dim3 grid((c.hidden / per_thread + 255) / 256, T);
     if (a.out_bf16) hipLaunchKernelGGL((k_merge<true>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((k_merge<false>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
