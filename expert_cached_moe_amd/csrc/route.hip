@@ -316,42 +316,58 @@ __global__ __launch_bounds__(kBlock) void k_perm_hist(const int32_t* __restrict_
     for (int e = tid; e < E; e += kBlock) hist[int64_t(c) * E + e] = s_cnt[e];
 }
 
-// counts, offsets, and base[chunk][e] = offsets[e] + pairs of e in earlier chunks.
-// Thread e walks its column of hist eight chunks at a time (independent loads in
-// flight), then the experts' totals are scanned.
+// counts, offsets, and base[chunk][e] = offsets[e] + pairs of e in earlier chunks.  The
+// workgroup's threads form G = 1024 / E groups per expert (thread e + E q: expert e, group q);
+// group q owns a contiguous range of chunks, sums its column of hist over that range in one
+// round of loads, and after the group partials and the experts' totals are scanned in LDS
+// writes its base values once (from the values still in registers when the range is at most
+// 8 chunks).  One thread per expert walking all the chunks took two dependent global round
+// trips per 8 chunks.
 __global__ __launch_bounds__(kBlock) void k_perm_scan(const int32_t* __restrict__ hist, int nchunks, int E,
                                                       int32_t* __restrict__ base, int32_t* __restrict__ counts,
                                                       int32_t* __restrict__ offsets) {
+    __shared__ int32_t s_part[kBlock];           // [G][E] partial sums
     __shared__ int32_t s_cnt[kMaxExperts];
     __shared__ int32_t s_off[kMaxExperts + 1];
     constexpr int U = 8;
     const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += kBlock) {
-        int run = 0;
-        for (int c0 = 0; c0 < nchunks; c0 += U) {
-            int h[U];
+    const int G = kBlock / E;                     // E <= 512, so G >= 2
+    const int span = (nchunks + G - 1) / G;       // chunks per group
+    const int e = tid % E, q = tid / E;
+    const bool act = q < G;
+    const int c0 = act ? q * span : 0, c1 = act ? min(nchunks, c0 + span) : 0;
+    int h[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) h[u] = c0 + u < nchunks ? hist[int64_t(c0 + u) * E + e] : 0;
+    for (int u = 0; u < U; ++u) h[u] = 0;
+    int part = 0;
+    for (int b = c0; b < c1; b += U) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (c0 + u < nchunks) base[int64_t(c0 + u) * E + e] = run;
-                run += h[u];
-            }
-        }
-        s_cnt[e] = run;
+        for (int u = 0; u < U; ++u) h[u] = b + u < c1 ? hist[int64_t(b + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) part += h[u];
+    }
+    if (act) s_part[q * E + e] = part;
+    __syncthreads();
+    for (int x = tid; x < E; x += kBlock) {
+        int total = 0;
+        for (int g = 0; g < G; ++g) total += s_part[g * E + x];
+        s_cnt[x] = total;
     }
     __syncthreads();
     wave0_scan(s_cnt, E, s_off, offsets, counts);
     __syncthreads();
-    for (int e = tid; e < E; e += kBlock) {
-        const int off = s_off[e];
-        for (int c0 = 0; c0 < nchunks; c0 += U) {
-            int b[U];
+    if (!act) return;
+    int run = s_off[e];
+    for (int g = 0; g < q; ++g) run += s_part[g * E + e];
+    for (int b = c0; b < c1; b += U) {
+        if (span > U) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) b[u] = c0 + u < nchunks ? base[int64_t(c0 + u) * E + e] : 0;
+            for (int u = 0; u < U; ++u) h[u] = b + u < c1 ? hist[int64_t(b + u) * E + e] : 0;
+        }
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (c0 + u < nchunks) base[int64_t(c0 + u) * E + e] = b[u] + off;
+        for (int u = 0; u < U; ++u) {
+            if (b + u < c1) base[int64_t(b + u) * E + e] = run;
+            run += h[u];
         }
     }
 }
