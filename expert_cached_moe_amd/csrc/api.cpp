@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <functional>
 #include <new>
 #include <string>
 #include <vector>
@@ -25,7 +26,9 @@ int hip_fail(moe_ctx* ctx, hipError_t e, const char* what) {
 int validate_config(const moe_config* c, std::string* why) {
     auto bad = [&](int code, const char* m) { if (why) *why = m; return code; };
     if (!c) return bad(MOE_EINVAL, "null config");
-    if (c->hidden <= 0 || c->hidden % 32) return bad(MOE_ESHAPE, "hidden must be a positive multiple of 32");
+    if (c->hidden <= 0 || c->hidden % 64) return bad(MOE_ESHAPE, "hidden must be a positive multiple of 64");
+    if (c->w_dtype == MOE_W_MXFP4 && c->hidden % 256)
+        return bad(MOE_ESHAPE, "hidden must be a multiple of 256 for MXFP4 weights");
     if (c->inter <= 0 || c->inter % 32) return bad(MOE_ESHAPE, "inter must be a positive multiple of 32");
     if (c->n_experts < 1 || c->n_experts > kMaxExperts) return bad(MOE_ESHAPE, "n_experts must be in 1..512");
     if (c->top_k < 1 || c->top_k > c->n_experts || c->top_k > kMaxTopK)
@@ -68,8 +71,7 @@ WsLayout ws_layout(const moe_config& c, int32_t max_T) {
     const int64_t pairs = T * c.top_k;
     const int64_t chunks = (pairs + kPermChunk - 1) / kPermChunk;
     const int64_t rows = pairs + (c.n_shared ? T : 0);
-    W.ctr = 0;
-    W.hist = align256(kCtrBytes);
+    W.hist = 0;
     W.base = align256(W.hist + chunks * c.n_experts * 4);
     W.tiles = align256(W.base + chunks * c.n_experts * 4);
     W.h = align256(W.tiles + gemm_tile_ints(c, int32_t(T)) * 4);
@@ -299,19 +301,20 @@ int moe_fill_wait(moe_ctx* ctx, hipStream_t s) {
     return e == hipSuccess ? MOE_OK : hip_fail(ctx, e, "hipStreamWaitEvent");
 }
 
-// Decode expert list from the host's copy of the top-k ids: per listed expert its tokens
-// (bit t) and each token's slot j among its k picks; the shared expert (last) takes all.
-// where[e] = index of expert e in h_experts or -1.
+// Decode expert list from the host's copy of the top-k ids: per listed expert that some
+// token of the step uses, its tokens (bit t) and each token's slot j among its k picks; the
+// shared expert (last) takes all.  Listed experts without a token produce no pair and are
+// left out, so the list holds at most T*k routed entries plus the shared one
+// (kMaxDecodeList), however many experts the caller lists.  where[e] = index of expert e in
+// h_experts or -1.
 static int build_decode_list(moe_ctx* ctx, int32_t T, const int32_t* h_topk_ids, const int32_t* h_experts,
-                             const int32_t* h_slots, int32_t n, int32_t with_shared, const std::vector<int32_t>& where,
+                             const int32_t* h_slots, int32_t with_shared, const std::vector<int32_t>& where,
                              DecodeList* dl) {
     const moe_config& c = ctx->cfg;
-    dl->n = n + (with_shared ? 1 : 0);
-    for (int i = 0; i < n; ++i) {
-        dl->ent[i] = h_experts[i] | (h_slots[i] << 10);
-        dl->tokmask[i] = 0;
-        dl->jpack[i] = 0;
-    }
+    if (T < 1 || T > kDecodeMaxT) return fail(ctx, MOE_ESHAPE, "decode list needs 1 <= T <= 8");
+    // list position of each listed expert with tokens, in first-use order (t, j)
+    std::vector<int32_t> pos(c.n_experts, -1);
+    dl->n = 0;
     for (int t = 0; t < T; ++t)
         for (int j = 0; j < c.top_k; ++j) {
             const int id = h_topk_ids[t * c.top_k + j];
@@ -320,10 +323,18 @@ static int build_decode_list(moe_ctx* ctx, int32_t T, const int32_t* h_topk_ids,
                 if (h_topk_ids[t * c.top_k + jj] == id) return fail(ctx, MOE_EINVAL, "repeated expert in a token");
             const int i = where[id];
             if (i < 0) continue;
-            dl->tokmask[i] |= 1u << t;
-            dl->jpack[i] |= uint32_t(j) << (4 * t);
+            if (pos[id] < 0) {
+                if (dl->n >= kMaxDecodeList - 1) return fail(ctx, MOE_ESHAPE, "decode list overflow");
+                pos[id] = dl->n++;
+                dl->ent[pos[id]] = h_experts[i] | (h_slots[i] << 10);
+                dl->tokmask[pos[id]] = 0;
+                dl->jpack[pos[id]] = 0;
+            }
+            dl->tokmask[pos[id]] |= 1u << t;
+            dl->jpack[pos[id]] |= uint32_t(j) << (4 * t);
         }
     if (with_shared) {
+        const int n = dl->n++;
         dl->ent[n] = kSharedTag;
         dl->tokmask[n] = (1u << T) - 1u;
         dl->jpack[n] = 0;
@@ -355,7 +366,7 @@ int moe_expert_ffn(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* h_to
     hipError_t e;
     if (host_lists) {
         DecodeList dl;
-        const int st = build_decode_list(ctx, T, h_topk_ids, h_experts, h_slots, n, with_shared, where, &dl);
+        const int st = build_decode_list(ctx, T, h_topk_ids, h_experts, h_slots, with_shared, where, &dl);
         if (st != MOE_OK) return st;
         e = launch_ffn_decode(c, ctx->lay, d_x, T, d_slot_base, d_shared, dl, d_o, d_ws, s);
         return e == hipSuccess ? MOE_OK : hip_fail(ctx, e, "moe_expert_ffn launch");
@@ -377,6 +388,21 @@ int moe_expert_ffn_merge(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t
                          const int32_t* d_topk_ids, const float* d_topk_w, const void* d_slot_base,
                          const int32_t* h_experts, const int32_t* h_slots, int32_t n, const void* d_shared,
                          int32_t with_shared, const float* d_y_host, void* d_out, void* d_ws, hipStream_t s) {
+    return moe::expert_ffn_merge(ctx, d_x, T, h_topk_ids, d_topk_ids, d_topk_w, d_slot_base, h_experts, h_slots, n,
+                                 d_shared, with_shared, d_y_host, d_out, [&](int32_t, void** ws) {
+                                     *ws = d_ws;
+                                     return d_ws ? MOE_OK : fail(ctx, MOE_EINVAL, "null workspace");
+                                 }, s);
+}
+
+}  // extern "C"
+
+namespace moe {
+
+int expert_ffn_merge(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* h_topk_ids, const int32_t* d_topk_ids,
+                     const float* d_topk_w, const void* d_slot_base, const int32_t* h_experts, const int32_t* h_slots,
+                     int32_t n, const void* d_shared, int32_t with_shared, const float* d_y_host, void* d_out,
+                     const std::function<int(int32_t, void**)>& workspace, hipStream_t s) {
     if (!ctx) return MOE_EINVAL;
     const moe_config& c = ctx->cfg;
     if (T < 0) return fail(ctx, MOE_EINVAL, "T < 0");
@@ -386,8 +412,8 @@ int moe_expert_ffn_merge(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t
     if (T == 0) return MOE_OK;
     if (T > kDecodeMaxT || !decode_shape_supported(c))
         return fail(ctx, MOE_ESHAPE, "moe_expert_ffn_merge takes decode batches (T <= 8) of the decode shapes");
-    if (!d_x || !d_out || !d_ws || !h_topk_ids || !d_topk_ids || !d_topk_w)
-        return fail(ctx, MOE_EINVAL, "null x/out/workspace/top-k argument");
+    if (!d_x || !d_out || !h_topk_ids || !d_topk_ids || !d_topk_w)
+        return fail(ctx, MOE_EINVAL, "null x/out/top-k argument");
     if (n > 0 && (!h_experts || !h_slots || !d_slot_base)) return fail(ctx, MOE_EINVAL, "null routed-expert argument");
     std::vector<int32_t> where(c.n_experts, -1);
     uint32_t mask[kMaxExperts / 32] = {0};
@@ -399,12 +425,19 @@ int moe_expert_ffn_merge(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t
         mask[e >> 5] |= 1u << (e & 31);
     }
     DecodeList dl;
-    const int st = build_decode_list(ctx, T, h_topk_ids, h_experts, h_slots, n, with_shared, where, &dl);
+    const int st = build_decode_list(ctx, T, h_topk_ids, h_experts, h_slots, with_shared, where, &dl);
     if (st != MOE_OK) return st;
+    void* d_ws = nullptr;
+    const int wst = workspace(T, &d_ws);     // after validation: an error leaves nothing behind
+    if (wst != MOE_OK) return wst;
     hipError_t e = launch_ffn_decode_merge(c, ctx->lay, d_x, T, d_slot_base, d_shared, dl, d_topk_ids, d_topk_w, mask,
                                            with_shared, d_y_host, d_out, d_ws, s);
     return e == hipSuccess ? MOE_OK : hip_fail(ctx, e, "moe_expert_ffn_merge launch");
 }
+
+}  // namespace moe
+
+extern "C" {
 
 int moe_merge_partial(moe_ctx* ctx, const void* d_o, const int32_t* d_topk_ids, const float* d_topk_w,
                       const int32_t* h_gpu_experts, int32_t n_gpu, int32_t with_shared, const float* d_y_host,

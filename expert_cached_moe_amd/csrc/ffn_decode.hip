@@ -671,6 +671,8 @@ hipError_t launch_ffn_decode_merge(const moe_config& c, const BlobLayout& lay, c
     // wave takes several experts one after another, and with 2 rows per workgroup (64 lanes
     // per row) the per-workgroup merge outweighs the saved launch; both run slower fused
     // than the separate down and merge kernels (pair outputs in the workspace).
+    // no listed expert has a token (and no shared expert): the output is the host part, or zero
+    if (list.n == 0) return launch_merge(c, nullptr, ids, w, mask, 0, y_host, T, out, s);
     int lpr = 64, cpl = 0;
     pick_down(ffn::chunks_per_row(c.w_dtype, c.inter), &lpr, &cpl);
     if (list.n <= kFusedWaves && c.top_k <= kFusedTopK && lpr <= 32)
@@ -686,6 +688,7 @@ hipError_t launch_ffn_decode_merge(const moe_config& c, const BlobLayout& lay, c
 hipError_t launch_ffn_decode(const moe_config& c, const BlobLayout& lay, const void* x, int32_t T,
                              const void* slot_base, const void* shared, const DecodeList& list, void* o, void* ws,
                              hipStream_t s) {
+    if (list.n == 0) return hipSuccess;       // no listed expert has a token: no pair output to write
     return launch_ffn_decode_impl(c, lay, x, T, slot_base, shared, list, o, ws, s, nullptr, nullptr, nullptr, 0,
                                   nullptr, nullptr);
 }

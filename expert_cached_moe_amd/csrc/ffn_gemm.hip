@@ -60,13 +60,12 @@ constexpr int kThreads = WM * WN * 64;
 constexpr int TM = BM / WM, TN = BN / WN;           // wave tile
 constexpr int FM = TM / MF, FN = TN / MF;           // MFMA tiles per wave
 constexpr int ACH = BM * 8 / kThreads;              // 16-byte A chunks per thread per K step
-constexpr int BCH = BN * 8 / kThreads;
 constexpr int FCH = BN * 2 / kThreads > 0 ? BN * 2 / kThreads : 1;  // MXFP4 code chunks per thread
 constexpr int LDS_STRIDE = BK + 8;                  // bf16 elements per LDS row (16-byte pad)
 constexpr int kStages = DB ? 2 : 1;
 constexpr int kLdsBytes = kStages * (BM + BN) * LDS_STRIDE * 2;
 constexpr int kXcds = 8;
-static_assert(ACH * kThreads == BM * 8 && BCH * kThreads == BN * 8, "chunking");
+static_assert(ACH * kThreads == BM * 8 && FCH * kThreads >= BN * 2, "chunking");
 static_assert(FM * MF == TM && FN * MF == TN, "wave tile");
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -182,10 +181,13 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// MODE 0: gate/up GEMM with SwiGLU epilogue; MODE 1: down GEMM.  FP4: MXFP4 weights.
-// WM x WN waves, each TM x TN = FM x FN MFMA tiles.  The next K step's global tiles
-// are loaded into registers while the current LDS stage is consumed.
-template <int MODE, bool FP4>
+// Register-staged GEMM for MXFP4 weights at shapes the large-tile kernel does not take
+// (K above the LDS room for a tile's scales, or K not a multiple of 128; bf16 weights always
+// run the pipelined or large-tile kernels).  MODE 0: gate/up GEMM with SwiGLU epilogue;
+// MODE 1: down GEMM.  WM x WN waves, each TM x TN = FM x FN MFMA tiles.  The next K step's
+// global tiles (A rows, weight codes and scales) are loaded into registers while the
+// current LDS stage is consumed; the codes are dequantised to bf16 on their way into LDS.
+template <int MODE>
 __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     uint16_t* As = lds;                                 // [stages][BM][LDS_STRIDE]
@@ -208,7 +210,8 @@ __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
     const int m0 = mt * BM, n0 = nt * BN;
     const int K = a.K;
 
-    // ---- per K step each thread moves ACH chunks of A and BCH of B (row = c / 8, 16-byte column c % 8)
+    // ---- per K step each thread moves ACH 16-byte chunks of A (row = c / 8, column c % 8) and FCH
+    //      16-byte runs of weight codes with their scale bytes (row = c / 2, half c % 2)
     const uint8_t* arow[ACH];
     bool avalid[ACH];
 #pragma unroll
@@ -225,11 +228,11 @@ __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
         }
         arow[i] = a.a_src + src_row * int64_t(K) * 2 + (c % 8) * 16;
     }
-    const int64_t wrow_bytes = FP4 ? K / 2 : int64_t(K) * 2;
+    const int64_t wrow_bytes = K / 2;
     const uint8_t* wbase = blob + a.off_w;
     const uint8_t* sbase = blob + a.off_s;
 
-    uint4 ra[ACH], rb[BCH];
+    uint4 ra[ACH];
     uint4 rbq[FCH];
     uint8_t rbs[FCH];
 
@@ -237,18 +240,11 @@ __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
     {                                                                                                        \
         _Pragma("unroll") for (int i = 0; i < ACH; ++i) ra[i] =                                              \
             avalid[i] ? *reinterpret_cast<const uint4*>(arow[i] + int64_t(k0) * 2) : make_uint4(0, 0, 0, 0); \
-        if (!FP4) {                                                                                          \
-            _Pragma("unroll") for (int i = 0; i < BCH; ++i) {                                                \
-                const int c = tid + kThreads * i;                                                            \
-                rb[i] = ffn::load_w(wbase + int64_t(n0 + c / 8) * wrow_bytes + int64_t(k0) * 2, c % 8);      \
-            }                                                                                                \
-        } else {                                                                                             \
-            _Pragma("unroll") for (int i = 0; i < FCH; ++i) {                                                \
-                const int c = tid + kThreads * i, r = c >> 1, half = c & 1;                                  \
-                if (c < BN * 2) {                                                                            \
-                    rbq[i] = *reinterpret_cast<const uint4*>(wbase + int64_t(n0 + r) * wrow_bytes + (k0) / 2 + half * 16); \
-                    rbs[i] = sbase[int64_t(n0 + r) * (K / 32) + (k0) / 32 + half];                           \
-                }                                                                                            \
+        _Pragma("unroll") for (int i = 0; i < FCH; ++i) {                                                    \
+            const int c = tid + kThreads * i, r = c >> 1, half = c & 1;                                      \
+            if (c < BN * 2) {                                                                                \
+                rbq[i] = *reinterpret_cast<const uint4*>(wbase + int64_t(n0 + r) * wrow_bytes + (k0) / 2 + half * 16); \
+                rbs[i] = sbase[int64_t(n0 + r) * (K / 32) + (k0) / 32 + half];                               \
             }                                                                                                \
         }                                                                                                    \
     }
@@ -260,20 +256,13 @@ __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
             const int c = tid + kThreads * i;                                                                \
             *reinterpret_cast<uint4*>(&as_[(c / 8) * LDS_STRIDE + (c % 8) * 8]) = ra[i];                     \
         }                                                                                                    \
-        if (!FP4) {                                                                                          \
-            _Pragma("unroll") for (int i = 0; i < BCH; ++i) {                                                \
-                const int c = tid + kThreads * i;                                                            \
-                *reinterpret_cast<uint4*>(&bs_[(c / 8) * LDS_STRIDE + (c % 8) * 8]) = rb[i];                 \
-            }                                                                                                \
-        } else {                                                                                             \
-            _Pragma("unroll") for (int i = 0; i < FCH; ++i) {                                                \
-                const int c = tid + kThreads * i, r = c >> 1, half = c & 1;                                  \
-                if (c < BN * 2) {                                                                            \
-                    uint4 v[4];                                                                              \
-                    fp4_to_bf16(rbq[i], rbs[i], v);                                                          \
-                    _Pragma("unroll") for (int q = 0; q < 4; ++q)                                            \
-                        *reinterpret_cast<uint4*>(&bs_[r * LDS_STRIDE + half * 32 + q * 8]) = v[q];          \
-                }                                                                                            \
+        _Pragma("unroll") for (int i = 0; i < FCH; ++i) {                                                    \
+            const int c = tid + kThreads * i, r = c >> 1, half = c & 1;                                      \
+            if (c < BN * 2) {                                                                                \
+                uint4 v[4];                                                                                  \
+                fp4_to_bf16(rbq[i], rbs[i], v);                                                              \
+                _Pragma("unroll") for (int q = 0; q < 4; ++q)                                                \
+                    *reinterpret_cast<uint4*>(&bs_[r * LDS_STRIDE + half * 32 + q * 8]) = v[q];              \
             }                                                                                                \
         }                                                                                                    \
     }
@@ -395,9 +384,6 @@ __global__ void __launch_bounds__(kThreads) k_gemm(const GemmArgs a) {
 // LDS rows are 64 bytes (4 chunks of 8 bf16); chunk c of row r is stored at slot
 // c ^ ((r >> 2) & 3), which keeps the 16 lanes of a fragment read on distinct banks.
 // A rows past the expert's end load row 0 of the expert (their outputs are dropped).
-#ifndef MOE_GEMM_DMA
-#define MOE_GEMM_DMA 1
-#endif
 #ifndef MOE_DMA_BM
 #define MOE_DMA_BM MOE_GEMM_BM
 #endif
@@ -675,9 +661,6 @@ __global__ void __launch_bounds__(dma::kThreads) k_gemm_dma(const GemmArgs a) {
 // one 16-byte LDS read gives a lane the codes of all four sub-steps and one scale covers
 // them; the codes become bf16 MFMA operands in registers (v_cvt_scalef32_pk_bf16_fp4,
 // exact: every e2m1 value times a power of two fits bf16).
-#ifndef MOE_GEMM_BIG
-#define MOE_GEMM_BIG 1
-#endif
 namespace big {
 #ifndef MOE_BIG_WN
 #define MOE_BIG_WN 4
@@ -1081,8 +1064,7 @@ k_gemm_big(const GemmArgs a) {
 // The GEMM stages use more than the default 64 KiB of LDS per workgroup.
 hipError_t allow_lds() {
     static hipError_t once = [] {
-        const void* ks[4] = {reinterpret_cast<const void*>(&k_gemm<0, false>), reinterpret_cast<const void*>(&k_gemm<0, true>),
-                             reinterpret_cast<const void*>(&k_gemm<1, false>), reinterpret_cast<const void*>(&k_gemm<1, true>)};
+        const void* ks[2] = {reinterpret_cast<const void*>(&k_gemm<0>), reinterpret_cast<const void*>(&k_gemm<1>)};
         for (const void* k : ks) {
             hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
             if (e != hipSuccess) return e;
@@ -1132,7 +1114,8 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     const WsLayout W = ws_layout(c, T);
     int32_t* tiles = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + W.tiles);
     const bool fp4 = c.w_dtype == MOE_W_MXFP4;
-    // kernel per GEMM: 2 large-tile, 1 pipelined 128 x 256, 0 register-staged (MXFP4 and other shapes).
+    // kernel per GEMM: 2 large-tile, 1 pipelined 128 x 256, 0 register-staged (MXFP4 shapes the
+    // large tile does not take; every bf16 shape gemm_shape_supported accepts fits the pipelined kernel).
     // The large tile needs long K loops to pay for its per-tile start and epilogue at one
     // workgroup per CU (measured on the 8K-token chunk of the 2048 x 768 layer: 547 us against
     // 643 us for GEMM 1 with K = 2048, about even for GEMM 2 with K = 768).
@@ -1140,13 +1123,11 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
         // large tile: an even slice count, A row offsets (rows of x or h times the row bytes)
         // in 32 bits and, for MXFP4, the tile's scales within their LDS region
         const int64_t a_rows = int64_t(T) * c.top_k + T;
-        const bool big_ok = MOE_GEMM_BIG && N % big::BN == 0 && K % (2 * big::BK) == 0 &&
+        const bool big_ok = N % big::BN == 0 && K % (2 * big::BK) == 0 &&
                             a_rows * K * 2 < (int64_t(1) << 32) && (!fp4 || K <= big::kMaxKFp4);
         if (fp4) return big_ok ? 2 : 0;
-        if (K < 2048 && MOE_GEMM_DMA && N % dma::BN == 0 && K % dma::BK == 0) return 1;
-        if (big_ok) return 2;
-        if (MOE_GEMM_DMA && N % dma::BN == 0 && K % dma::BK == 0) return 1;
-        return 0;
+        if (K >= 2048 && big_ok) return 2;
+        return 1;
     };
     auto bm_of = [](int kd) { return kd == 2 ? big::BM : kd == 1 ? dma::BM : BM; };
     const int kind1 = kind(2 * c.inter, c.hidden), kind2 = kind(c.hidden, c.inter);
@@ -1200,16 +1181,12 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
                 hipLaunchKernelGGL((k_gemm_dma<0>), dim3(a.grid), dim3(dma::kThreads), dma::kLdsBytes, s, a);
             else
                 hipLaunchKernelGGL((k_gemm_dma<1>), dim3(a.grid), dim3(dma::kThreads), dma::kLdsBytes, s, a);
-        } else if (fp4) {
-            if (mode == 0)
-                hipLaunchKernelGGL((k_gemm<0, true>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
-            else
-                hipLaunchKernelGGL((k_gemm<1, true>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
         } else {
+            if (!fp4) return hipErrorInvalidValue;          // the register-staged kernel takes MXFP4 only
             if (mode == 0)
-                hipLaunchKernelGGL((k_gemm<0, false>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
+                hipLaunchKernelGGL((k_gemm<0>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
             else
-                hipLaunchKernelGGL((k_gemm<1, false>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
+                hipLaunchKernelGGL((k_gemm<1>), dim3(a.grid), dim3(kThreads), kLdsBytes, s, a);
         }
         return hipGetLastError();
     };

@@ -38,14 +38,14 @@ int validate_config(const moe_config* c, std::string* why);
 BlobLayout blob_layout(const moe_config& c);
 inline int act_bytes(const moe_config& c) { return c.w_dtype == MOE_W_F32 ? 4 : 2; }
 
-// Scratch layout inside the caller's workspace.
-// The counter block sits at offset 0 (same address for every T): it must be zero
-// before the first call and every call leaves it zeroed.
+// Scratch layout inside the caller's workspace (pure scratch: nothing in it needs a value
+// before a call).  hist/base: permutation histograms of the large-T route; tiles: the grouped
+// GEMM's tile list; h: SwiGLU activations; o: decode pair outputs of moe_expert_ffn_merge
+// when its down projection and merge run as separate kernels.
 struct WsLayout {
-    int64_t ctr = 0, hist = 0, base = 0, tiles = 0, h = 0, o = 0, bytes = 0;
+    int64_t hist = 0, base = 0, tiles = 0, h = 0, o = 0, bytes = 0;
 };
 int64_t gemm_tile_ints(const moe_config& c, int32_t T);  // tile-list entries of the grouped GEMM
-constexpr int64_t kCtrBytes = 4 * (2 + kMaxExperts + 1 + 61);  // ticket, finished, per-entry counts
 WsLayout ws_layout(const moe_config& c, int32_t max_T);
 
 // A small persistent worker pool for the host FFN.
@@ -98,6 +98,13 @@ namespace moe {
 
 int fail(moe_ctx* ctx, int code, const std::string& msg);
 int hip_fail(moe_ctx* ctx, hipError_t e, const char* what);
+
+// moe_expert_ffn_merge with the workspace supplied by `workspace(T, &ptr)` once the arguments
+// are valid; a status other than MOE_OK from it is returned as is (it sets the message).
+int expert_ffn_merge(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* h_topk_ids, const int32_t* d_topk_ids,
+                     const float* d_topk_w, const void* d_slot_base, const int32_t* h_experts, const int32_t* h_slots,
+                     int32_t n, const void* d_shared, int32_t with_shared, const float* d_y_host, void* d_out,
+                     const std::function<int(int32_t, void**)>& workspace, hipStream_t s);
 
 // ---- kernel launchers (defined in the .hip files) ----
 struct ExpertList {

@@ -20,7 +20,7 @@ class LayerBuffers:
         self.max_T = max_T
         self.blob_bytes = B.moe_expert_bytes(cfg)
         dev = torch.device(device)
-        self.ws = torch.zeros(B.moe_workspace_bytes(cfg, max_T), dtype=torch.uint8, device=dev)  # counters start at 0
+        self.ws = torch.empty(B.moe_workspace_bytes(cfg, max_T), dtype=torch.uint8, device=dev)
         n = max(1, max_T * self.k)
         self.ids = torch.empty(n, dtype=torch.int32, device=dev)
         self.w = torch.empty(n, dtype=torch.float32, device=dev)

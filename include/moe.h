@@ -140,10 +140,8 @@ const char* moe_status_string(int status);
  * ([B] "Elastic Memory": experts are read into their final host layout). */
 int64_t moe_expert_bytes(const moe_config* cfg);
 /* Device scratch bytes needed by moe_route + moe_expert_ffn (+ moe_expert_ffn_merge) for
- * up to max_T tokens.
- * The workspace must be zero-filled once before its first use; every call leaves
- * its first kilobytes (queue counters of the decode FFN) zeroed again, the rest is
- * scratch.  Calls that share a workspace must be ordered (one stream, or events). */
+ * up to max_T tokens.  The workspace is scratch (caller-owned, no initial value needed);
+ * calls that share a workspace must be ordered (one stream, or events). */
 int64_t moe_workspace_bytes(const moe_config* cfg, int32_t max_T);
 /* Rows of the pair-output buffer d_o for T tokens: T*k (+ T with a shared expert).  Each
  * row holds H values in the activation dtype (fp32 for fp32 weights, else bf16). */
@@ -157,12 +155,19 @@ int64_t moe_pair_rows(const moe_config* cfg, int32_t T);
 int moe_pack_expert(const moe_config* cfg, const void* wg, const void* wu, const void* wd,
                     const uint8_t* sg, const uint8_t* su, const uint8_t* sd, void* blob);
 
-/* Bind the pools used by moe_fill and moe_host_ffn.
- *   d_slots: device, n_slots blobs (n_slots <= cfg->n_slots);
+/* Bind the pools used by moe_fill and moe_host_ffn ([A] "Abandoning fixed offloading ...":
+ * a GPU expert cache of limited capacity in front of the full expert pool in host memory;
+ * [B] "Elastic Memory": the host copy is kept in its final layout, and the GPU holds as
+ * many expert slots as its memory budget allows).
+ *   d_slots: device, n_slots blobs (n_slots <= cfg->n_slots), caller-owned; slot i is
+ *            the blob at d_slots + i*moe_expert_bytes;
  *   h_pool:  host (pinned for asynchronous fills), n_pool = n_layers*E blobs in
- *            key order (layer*E + expert).
- * Either pointer may be NULL when the corresponding calls are not used.  Makes no
- * HIP call (the fill event is created by the first moe_fill / moe_upload). */
+ *            key order (layer*E + expert), caller-owned.
+ * The library keeps the pointers, never frees them, and reads / writes them only in
+ * moe_fill, moe_move_slots, moe_prefill_stream and moe_host_ffn.  Either pointer may be
+ * NULL when the corresponding calls are not used.  Errors (no state change): MOE_EINVAL
+ * (n_slots out of range, a device pool missing, n_pool != n_layers*E).  Makes no HIP call
+ * (the fill event is created by the first moe_fill / moe_upload). */
 int moe_bind_pools(moe_ctx* ctx, void* d_slots, int32_t n_slots, const void* h_pool, int32_t n_pool);
 
 /* ---------------------------------------------------------------- router */
@@ -189,13 +194,20 @@ int moe_route(moe_ctx* ctx, const float* d_logits, int32_t T, int32_t* d_topk_id
 int32_t moe_qstar(int32_t m, double bp, double bh, int32_t rounding);
 /* Plan one decode step of `layer` from the host copy of its top-k ids
  * h_topk_ids [T][k] and update the cache: hits, q* fills (evicting the least
- * recently used expert not used in this step), host set.  Synchronous, host only.
- * Errors (no state change): MOE_EINVAL (ids out of range or repeated within a
- * token, bad layer), MOE_ECAPACITY (plan->cap too small). */
+ * recently used expert not used in this step), host set.  ([A] "Abandoning fixed
+ * offloading ...": the decode cache is one LRU over the experts of all layers, updated on
+ * misses; [B] "The q* Policy": of the m misses, about m*B_P/B_H are copied to the GPU and
+ * the rest computed on the CPU; [B] "Elastic Memory": the cache starts empty.)  The ids
+ * are caller-owned and only read; the plan's arrays are caller-owned and written.
+ * Synchronous, host only.  Errors (no state change): MOE_EINVAL (ids out of range or
+ * repeated within a token, bad layer), MOE_ECAPACITY (plan->cap too small). */
 int moe_lru_step(moe_ctx* ctx, int32_t layer, const int32_t* h_topk_ids, int32_t T, moe_plan* plan);
-/* Replay n_steps decode steps (ids [n_steps][T][k]) in order; plans may be NULL
- * (then only *stats is filled), else an array of n_steps plans.  stats may be NULL.
- * All ids are validated before the cache is touched. */
+/* Replay n_steps decode steps of `layer` (ids [n_steps][T][k], host, read only) in order,
+ * exactly as n_steps calls of moe_lru_step would ([A] "Abandoning fixed offloading ...":
+ * the pages measure their miss rates by replaying routing traces against the cache).
+ * plans may be NULL (then only *stats is filled), else a caller-owned array of n_steps
+ * plans; stats (may be NULL) receives the cumulative statistics after the replay.  All ids
+ * are validated before the cache is touched (errors as moe_lru_step, no state change). */
 int moe_lru_replay(moe_ctx* ctx, int32_t layer, const int32_t* h_topk_ids, int32_t n_steps, int32_t T,
                    moe_plan* plans, moe_stats* stats);
 /* Empty the cache (cold start) and zero the statistics. */
@@ -232,14 +244,17 @@ int moe_fill_wait(moe_ctx* ctx, hipStream_t s);
 int moe_upload(moe_ctx* ctx, void* d_dst, const void* h_src, int64_t bytes, hipStream_t side);
 
 /* ---------------------------------------------------------------- expert FFN */
-/* GPU SwiGLU experts over device slots (async on s):
+/* GPU SwiGLU experts over device slots (async on s) ([B] "Sparsity Is a Lie": each routed
+ * expert is a small feed-forward network; [B] "The q* Policy": experts resident in the GPU
+ * cache, or just copied there, are computed on the GPU):
  *   o[p] = Wd_e (silu(Wg_e x_t) * (Wu_e x_t)) for every pair p = t*k + j whose
  *   expert e = topk_ids[t][j] is listed in h_experts, read from the blob at
  *   d_slot_base + h_slots[i]*moe_expert_bytes; with with_shared = 1 also
  *   o[T*k + t] for the shared expert blob d_shared (all tokens).
  *   d_x [T][H] activations; h_experts / h_slots: host arrays of n (<= E) distinct
- *   expert ids and slot indices; d_o [moe_pair_rows][H] in the activation dtype,
- *   each pair's result rounded once (rows of unlisted experts are not written);
+ *   expert ids and slot indices (listed experts that no token uses are skipped);
+ *   d_o [moe_pair_rows][H] in the activation dtype, each pair's result rounded once
+ *   (rows of unlisted experts are not written);
  *   d_ws: moe_workspace_bytes(max_T >= T).
  *   Which tokens use an expert comes from h_topk_ids (host copy [T][k] of the
  *   step's ids, as moe_lru_step consumes) when given and T <= 8; the kernels then

@@ -15,21 +15,22 @@ def config(wl, n_slots=None, bp=52.7, bh=77.3, n_layers=1, q_round=0, renormaliz
 
 
 class Experts:
-    """Lazily drawn expert weights of a workload (natural layout and fp64 for the oracle)."""
+    """Lazily drawn expert weights of one MoE layer of a workload (natural layout and fp64 for the oracle)."""
 
-    def __init__(self, wl):
+    def __init__(self, wl, layer=0):
         self.wl = wl
+        self.layer = layer
         self._raw = {}
         self._f64 = {}
 
     def prefetch(self, es, threads=8):
         need = [e for e in es if e not in self._raw]
         if need:
-            self._raw.update(synth.expert_weights_many(self.wl, need, threads))
+            self._raw.update(synth.expert_weights_many(self.wl, need, threads, layer=self.layer))
 
     def raw(self, e):
         if e not in self._raw:
-            self._raw[e] = synth.expert_weights(self.wl, e)
+            self._raw[e] = synth.expert_weights(self.wl, e, layer=self.layer)
         return self._raw[e]
 
     def f64(self, e):

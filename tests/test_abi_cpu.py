@@ -41,7 +41,7 @@ def test_config_validation():
     ok = B.make_config(256, 128, 8, 2, 0, 3, 1, 0)
     B.moe_destroy(B.moe_create(ok))
     bad = [
-        dict(hidden=100), dict(inter=48), dict(n_experts=0), dict(n_experts=513), dict(top_k=9),
+        dict(hidden=100), dict(hidden=96), dict(hidden=224, w_dtype=2), dict(inter=48), dict(n_experts=0), dict(n_experts=513), dict(top_k=9),
         dict(top_k=0), dict(n_shared=2), dict(n_slots=-1), dict(n_layers=0), dict(w_dtype=7),
         dict(renormalize=2), dict(q_round=5), dict(bp_gbps=0.0), dict(bh_gbps=float("nan")),
     ]
@@ -250,6 +250,40 @@ def test_multilayer_keys():
         assert p.get("fill_victim").tolist() == want["fill_victim"]
         assert p.get("hit").tolist() == want["hit"]
         assert np.array_equal(p.get("slot_of_expert"), want["slot_of_expert"])
+    B.moe_destroy(ctx)
+
+
+@pytest.mark.parametrize("name,n_layers,B_,steps", [("a3b_decode_bf16", 4, 1, 384), ("v4flash_decode_bf16", 4, 2, 256),
+                                                    ("a3b_decode_bf16", 8, 1, 128)])
+def test_multilayer_stack_matches_oracle(name, n_layers, B_, steps):
+    """A stack of n_layers MoE layers shares one cache whose capacity is the workload's fraction
+    of the whole pool (37 % or 11 % of n_layers * E), keyed (layer, expert) ([A] "Abandoning
+    fixed offloading ...": one LRU over the experts of all layers).  Each layer routes by its own
+    Zipf trace; every decode step plans layer 0 .. n_layers-1 in order.  Every plan, the slot
+    tables and the statistics match the oracle's cache bit for bit."""
+    wl = synth.workload(name)
+    frac = wl.C / wl.E
+    C = int(round(frac * n_layers * wl.E))
+    cfg = config(wl, n_slots=C, n_layers=n_layers)
+    ctx = B.moe_create(cfg)
+    ref = oracle.LRUCache(C, wl.E, n_layers=n_layers)
+    traces = [synth.zipf_reuse_trace(wl, B_, steps, tag=100 + l)[0] for l in range(n_layers)]
+    p = B.Plan(min(wl.E, B_ * wl.k), wl.E)
+    misses = distinct = 0
+    for s in range(steps):
+        for l in range(n_layers):
+            ids = oracle.route(traces[l][s], wl.k)[0]
+            B.moe_lru_step(ctx, l, ids, B_, p)
+            want = ref.step(ids, 52.7, 77.3, layer=l)
+            for f in ("distinct", "hit", "hit_slot", "fill", "fill_slot", "fill_victim", "host"):
+                assert p.get(f).tolist() == list(want[f]), (s, l, f)
+            assert np.array_equal(p.get("slot_of_expert"), want["slot_of_expert"]), (s, l)
+            misses += want["m"]
+            distinct += len(want["distinct"])
+    for l in range(n_layers):
+        assert np.array_equal(B.moe_lru_slots(ctx, l, wl.E), ref.slot_table(l))
+    st = B.moe_lru_stats(ctx)
+    assert (st.misses, st.distinct, st.steps) == (misses, distinct, steps * n_layers)
     B.moe_destroy(ctx)
 
 

@@ -14,7 +14,7 @@ import torch
 import oracle
 import synth
 from helpers import TOL, config, dev_act, out_f64, rel_err_rows
-from test_gpu_parity import GpuLayer, _route_case
+from test_gpu_parity import GpuLayer, _route_case, check_route
 
 pytestmark = pytest.mark.gpu
 
@@ -48,9 +48,9 @@ def test_prefill_listed_experts_without_tokens(B):
     G = GpuLayer(B, wl, allx, T)
     x = synth.activations(wl, T, tag=77)
     out = G.run(logits, x, allx, 0)
+    ids, gates = check_route(G, logits, T)
     y = out_f64(out, wl, T)
-    g32 = G.L.w[: T * wl.k].cpu().numpy().reshape(T, wl.k).astype(np.float64)
-    ref = oracle.moe_layer(oracle.act_f64(x, wl.act_dtype), ids, g32, G.ex)
+    ref = oracle.moe_layer(oracle.act_f64(x, wl.act_dtype), ids, gates, G.ex)
     assert rel_err_rows(y, ref).max() <= TOL[wl.wdtype]
     assert len(set(ids.ravel().tolist())) < wl.E                # some listed experts had no token
     G.L.close()
@@ -79,10 +79,40 @@ def test_decode_overlap_extremes(B, name, mode):
     x = synth.activations(wl, T, tag=5)
     ws = 1 if wl.n_shared else 0
     out = G.run(logits, x, present, ws)
+    ids, gates = check_route(G, logits, T)
     y = out_f64(out, wl, T)
-    g32 = G.L.w[: T * wl.k].cpu().numpy().reshape(T, wl.k).astype(np.float64)
-    ref = oracle.moe_layer(oracle.act_f64(x, wl.act_dtype), ids, g32, G.ex, shared=G.ex.f64(wl.E) if ws else None)
+    ref = oracle.moe_layer(oracle.act_f64(x, wl.act_dtype), ids, gates, G.ex, shared=G.ex.f64(wl.E) if ws else None)
     assert rel_err_rows(y, ref).max() <= TOL[wl.wdtype]
+    G.L.close()
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_decode_lists_every_expert(B, T):
+    """The caller lists all 512 experts of a layer (every one resident) for a decode batch of
+    top-16 routing: only experts some token uses are computed (at most T * k = 128 of them),
+    the listed experts without a token add nothing and their pair rows stay unwritten; the
+    one-call path (experts + merge) is bit-identical to the two calls."""
+    print(f"[decode-every-expert] E=512 k=16 T={T}", flush=True)
+    from test_gpu_parity import pair_rows_written
+    base = synth.workload("a3b_decode_bf16")
+    wl = dataclasses.replace(base, name="bf16_512x256_e512_k16", H=512, I=256, E=512, k=16, C=512)
+    logits = synth.iid_logits(wl, T, tag=40 + T)
+    allx = list(range(wl.E))
+    G = GpuLayer(B, wl, allx, T)
+    x = synth.activations(wl, T, tag=40 + T)
+    out = G.run(logits, x, allx, 0)
+    ids, gates = check_route(G, logits, T)
+    o = pair_rows_written(G, T, ids, set(allx), 0)
+    y = out_f64(out, wl, T)
+    xf = oracle.act_f64(x, wl.act_dtype)
+    ref = oracle.moe_layer(xf, ids, gates, G.ex)
+    assert rel_err_rows(y, ref).max() <= TOL[wl.wdtype]
+    assert np.isfinite(o).all()
+    dx = dev_act(x)
+    one = torch.full_like(out, 7)
+    G.L.ffn_merge(dx, T, G.pool, allx, allx, ids, None, 0, None, one)
+    torch.cuda.synchronize()
+    assert torch.equal(one, out)
     G.L.close()
 
 

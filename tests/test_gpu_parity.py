@@ -5,6 +5,8 @@ plans) must match bit for bit; gates within 1e-6 relative; layer outputs within
 the per-token relative error max|y - y_ref| / max|y_ref| of 1e-5 (fp32) or 2e-2
 (bf16, MXFP4), with a tighter secondary bound where the arithmetic allows it.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -109,6 +111,44 @@ def test_route_parity(B, case):
         _route_case(B, wl, np.random.default_rng(0).standard_normal((9, 8)).astype(np.float32))
 
 
+# bf16 / fp32-high-half bit pattern of a quiet NaN, written into the pair outputs before a call
+POISON = 0x7FC1
+
+
+def check_route(G, logits, T):
+    """The GPU's ids of the last route equal the oracle's bit for bit and its gates agree within
+    1e-6 relative; returns the oracle's (ids, gates), from which every reference is built."""
+    k = G.wl.k
+    ids = G.L.ids[: T * k].cpu().numpy().reshape(T, k)
+    w = G.L.w[: T * k].cpu().numpy().reshape(T, k)
+    rids, rg = oracle.route(logits, k)
+    assert np.array_equal(ids, rids), "top-k ids differ from the oracle"
+    assert np.abs(w - rg).max() <= 1e-6 * np.abs(rg).max() + 1e-12, "gates differ from the oracle"
+    return rids, rg
+
+
+def pair_rows_written(G, T, ids, gpu, with_shared):
+    """Pair-output rows of listed experts (and the shared expert's rows) as fp64; asserts every
+    other row still holds the poison pattern (the call writes only its listed experts' pairs)."""
+    wl = G.wl
+    rows = T * wl.k + (T if with_shared else 0)
+    raw = G.L.o.view(torch.int16)[: rows * wl.H * (2 if wl.act_dtype == "f32" else 1)].cpu().numpy()
+    raw = raw.reshape(rows, -1)
+    listed = np.zeros(rows, bool)
+    for t in range(T):
+        for j in range(wl.k):
+            listed[t * wl.k + j] = int(ids[t, j]) in gpu
+    listed[T * wl.k:] = True
+    assert (raw[~listed] == POISON).all(), "pair rows of unlisted experts were written"
+    out = np.full((rows, wl.H), np.nan)
+    got = np.ascontiguousarray(raw[listed])
+    if wl.act_dtype == "f32":
+        out[listed] = got.view(np.float32).astype(np.float64)
+    else:
+        out[listed] = oracle.bf16_bits_to_f64(got.view(np.uint16))
+    return out
+
+
 class GpuLayer:
     """Device pool of packed experts (slot = position in ``experts``) and buffers."""
 
@@ -128,9 +168,11 @@ class GpuLayer:
 
     def run(self, logits, x, gpu_experts, with_shared, y_host=None, host_ids=True):
         """host_ids: decode token lists from the host copy of the ids (else from the router's
-        device offsets/permutation)."""
+        device offsets/permutation).  The pair-output buffer is filled with POISON first, so
+        rows the call must not write can be checked afterwards."""
         T = logits.shape[0]
         wl, L = self.wl, self.L
+        L.o.view(torch.int16).fill_(POISON)
         L.route(torch.from_numpy(np.ascontiguousarray(logits)).cuda(), T)
         h_ids = L.ids[: T * wl.k].cpu().numpy().reshape(T, wl.k) if host_ids else None
         dx = _dev_act(x)
@@ -156,17 +198,21 @@ def _decode_case(B, name, T, frac, seed, host_ids=True, wl=None):
     x = synth.activations(wl, T, tag=seed)
     ws = 1 if wl.n_shared else 0
     out = G.run(logits, x, gpu, ws, host_ids=host_ids)
+    check_route(G, logits, T)
     y = _out_f64(out, wl, T)
     xf = oracle.act_f64(x, wl.act_dtype)
-    g32 = G.L.w[: T * wl.k].cpu().numpy().reshape(T, wl.k).astype(np.float64)
     shared = G.ex.f64(wl.E) if wl.n_shared else None
-    ref = oracle.moe_layer(xf, ids, g32, G.ex, shared=shared, subset=set(gpu))
+    ref = oracle.moe_layer(xf, ids, gates, G.ex, shared=shared, subset=set(gpu))
     err = rel_err_rows(y, ref)
     tol = TOL[wl.wdtype]
     assert err.max() <= tol, (name, T, err.max())
-    # per-pair expert outputs (activation dtype, before the gate-weighted sum): tighter bound
-    rows = T * wl.k + (T if ws else 0)
-    o = out_f64(G.L.o[: rows * wl.H], wl, rows)
+    # per-pair expert outputs (activation dtype, before the gate-weighted sum): tighter bound;
+    # rows of experts not on the GPU must be untouched
+    o = pair_rows_written(G, T, ids, set(gpu), ws)
+    if ws:
+        r = oracle.expert_ffn(shared, xf)
+        pe = rel_err_rows(o[T * wl.k:], r).max()
+        assert pe <= (1e-5 if wl.wdtype == "f32" else 1.5e-2), (name, "shared", pe)
     for t in range(T):
         for j in range(wl.k):
             e = int(ids[t, j])
@@ -254,12 +300,35 @@ def test_small_prefill_parity(B, name, T):
     x = synth.activations(wl, T, tag=T)
     ws = 1 if wl.n_shared else 0
     out = G.run(logits, x, present, ws)
+    ids, gates = check_route(G, logits, T)
     y = _out_f64(out, wl, T)
-    g32 = G.L.w[: T * wl.k].cpu().numpy().reshape(T, wl.k).astype(np.float64)
-    ref = oracle.moe_layer(oracle.act_f64(x, wl.act_dtype), ids, g32, G.ex,
+    ref = oracle.moe_layer(oracle.act_f64(x, wl.act_dtype), ids, gates, G.ex,
                            shared=G.ex.f64(wl.E) if ws else None)
     err = rel_err_rows(y, ref)
     assert err.max() <= TOL[wl.wdtype], err.max()
+    G.L.close()
+
+
+@pytest.mark.parametrize("H,I", [(8192, 512), (512, 4224)])
+def test_prefill_mxfp4_register_staged(B, H, I):
+    """MXFP4 GEMM shapes the large-tile kernel does not take run the register-staged kernel:
+    a gate/up reduction of K = 8192 (the tile's scales would not fit its LDS region) and a
+    down reduction of K = 4224 (the same).  Ragged 40-token batch, shared expert included."""
+    print(f"[prefill-mxfp4-staged] H={H} I={I}", flush=True)
+    base = synth.workload("v4flash_mxfp4")
+    wl = dataclasses.replace(base, name=f"mxfp4_{H}x{I}", H=H, I=I, E=8, k=2, C=8, T=40)
+    T = wl.T
+    logits = synth.iid_logits(wl, T, tag=T)
+    present = sorted(set(oracle.route(logits, wl.k)[0].ravel().tolist()))
+    G = GpuLayer(B, wl, present, T)
+    x = synth.activations(wl, T, tag=T)
+    out = G.run(logits, x, present, 1)
+    ids, gates = check_route(G, logits, T)
+    y = _out_f64(out, wl, T)
+    ref = oracle.moe_layer(oracle.act_f64(x, wl.act_dtype), ids, gates, G.ex, shared=G.ex.f64(wl.E))
+    err = rel_err_rows(y, ref)
+    assert err.max() <= TOL[wl.wdtype], err.max()
+    assert np.median(err) <= 6e-3, np.median(err)
     G.L.close()
 
 
@@ -277,15 +346,12 @@ def test_prefill_full_size_sampled(B, name, n_sample):
     ws = 1 if wl.n_shared else 0
     out = G.run(logits, x, list(range(wl.E)), ws)
     y = _out_f64(out, wl, T)
-    ids = G.L.ids[: T * wl.k].cpu().numpy().reshape(T, wl.k)
-    rids, _ = oracle.route(logits, wl.k)
-    assert np.array_equal(ids, rids)
-    g32 = G.L.w[: T * wl.k].cpu().numpy().reshape(T, wl.k).astype(np.float64)
+    rids, rg = check_route(G, logits, T)
     rng = np.random.default_rng(0)
     sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_sample - 2, replace=False)]))
     xs = oracle.act_f64(x[sample], wl.act_dtype)
     conv = lambda e: oracle.expert_f64(ex.raw(e), wl.wdtype)          # no fp64 cache: bounded memory
-    ref = oracle.moe_layer(xs, rids[sample], g32[sample], conv, shared=conv(wl.E) if ws else None)
+    ref = oracle.moe_layer(xs, rids[sample], rg[sample], conv, shared=conv(wl.E) if ws else None)
     err = rel_err_rows(y[sample], ref)
     assert err.max() <= TOL[wl.wdtype], err.max()
     # typical error of two bf16 roundings (h, then each pair output, up to 2^-9 relative

@@ -37,13 +37,13 @@ def _act_tensor(wl, n):
 
 
 # ---------------------------------------------------------------- cached decode
-def _decode_inputs(wl, Bt, n_steps):
+def _decode_inputs(wl, Bt, n_steps, layer=0):
     if wl.name == "tiny_fp32":
         # the tiny layer routes with its own router: logits = x . W_r, one token per step
         x = synth.activations(wl, n_steps * Bt, tag=21)
         logits = oracle.router_logits(x, synth.router_weights(wl)).astype(np.float32)
         return logits.reshape(n_steps, Bt, wl.E), x
-    logits, _ = synth.zipf_reuse_trace(wl, Bt, n_steps)
+    logits, _ = synth.zipf_reuse_trace(wl, Bt, n_steps, tag=0 if layer == 0 else 100 + layer)
     return logits, synth.activations(wl, n_steps * Bt, tag=11)
 
 
@@ -61,35 +61,52 @@ def test_cached_decode_pipeline_resize(B):
     _run_pipeline(B, "a3b_decode_bf16", 4, 24, resizes={8: 20, 16: 47})
 
 
-def _run_pipeline(B, name, Bt, n_steps, resizes=None):
+@pytest.mark.parametrize("name,n_layers,Bt,n_steps", [("a3b_decode_bf16", 4, 1, 10), ("v4flash_mxfp4", 4, 2, 4)])
+def test_cached_decode_pipeline_layer_stack(B, name, n_layers, Bt, n_steps):
+    """One cache over a stack of MoE layers ([A] "Abandoning fixed offloading ...": a single
+    LRU spans the experts of all layers): the slot pool holds the workload's fraction of the
+    whole pool (37 % or 11 % of n_layers * E blobs), the host pool every (layer, expert) blob
+    in key order, each layer has its own weights and routing trace, and every decode step
+    runs layer 0 .. n_layers-1 through the pipeline with plans keyed (layer, expert)."""
+    _run_pipeline(B, name, Bt, n_steps, n_layers=n_layers)
+
+
+def _run_pipeline(B, name, Bt, n_steps, resizes=None, n_layers=1):
     from expert_cached_moe_amd.runtime import LayerBuffers, pack_pool
-    print(f"[pipeline] {name} B={Bt} steps={n_steps} resizes={resizes}", flush=True)
+    print(f"[pipeline] {name} B={Bt} steps={n_steps} layers={n_layers} resizes={resizes}", flush=True)
     wl = synth.workload(name)
-    E, k, H = wl.E, wl.k, wl.H
-    logits, x = _decode_inputs(wl, Bt, n_steps)
-    used = sorted({int(e) for s in range(n_steps) for e in oracle.route(logits[s], k)[0].ravel()})
-    ex = Experts(wl)
-    ex.prefetch(used + ([E] if wl.n_shared else []), threads=16)
-    cfg = config(wl)
+    E, k, H, NL = wl.E, wl.k, wl.H, n_layers
+    C = wl.C if NL == 1 else int(round(wl.C / E * NL * E))
+    inputs = [_decode_inputs(wl, Bt, n_steps, layer=l) for l in range(NL)]
+    logits = [inp[0] for inp in inputs]
+    x = inputs[0][1]                                   # every layer takes the same x
+    routes = [[oracle.route(logits[l][s], k) for s in range(n_steps)] for l in range(NL)]
+    exs = []
+    for l in range(NL):
+        used = sorted({int(e) for s in range(n_steps) for e in routes[l][s][0].ravel()})
+        ex = Experts(wl, layer=l)
+        ex.prefetch(used + ([E] if wl.n_shared else []), threads=16)
+        exs.append((ex, set(used)))
+    cfg = config(wl, n_slots=C, n_layers=NL)
     nb = B.moe_expert_bytes(cfg)
-    host_pool = pack_pool(cfg, [ex.raw(e) if e in used else None for e in range(E)], pin=True)
-    slots = torch.full((wl.C * nb,), 0xFF, dtype=torch.uint8, device="cuda")
-    shared = pack_pool(cfg, [ex.raw(E)], pin=False).cuda() if wl.n_shared else None
+    host_pool = pack_pool(cfg, [ex.raw(e) if e in used else None for ex, used in exs for e in range(E)], pin=True)
+    slots = torch.full((C * nb,), 0xFF, dtype=torch.uint8, device="cuda")
+    shared = [pack_pool(cfg, [ex.raw(E)], pin=False).cuda() for ex, _ in exs] if wl.n_shared else None
     ws = 1 if wl.n_shared else 0
     L = LayerBuffers(cfg, Bt)
-    B.moe_bind_pools(L.ctx, slots, wl.C, host_pool, E)
-    d_logits = torch.from_numpy(np.ascontiguousarray(logits.reshape(n_steps * Bt, E), np.float32)).cuda()
+    B.moe_bind_pools(L.ctx, slots, C, host_pool, NL * E)
+    d_logits = [torch.from_numpy(np.ascontiguousarray(lg.reshape(n_steps * Bt, E), np.float32)).cuda()
+                for lg in logits]
     d_x = dev_act(x)
     h_x = torch.empty(Bt * H, dtype=d_x.dtype, pin_memory=True)
     h_y = torch.zeros(Bt * H, dtype=torch.float32, pin_memory=True)
     d_y = torch.empty(Bt * H, dtype=torch.float32, device="cuda")
     out = _act_tensor(wl, Bt * H)
     plan = B.Plan(min(E, Bt * k), E)
-    ref_cache = oracle.LRUCache(wl.C, E)
+    ref_cache = oracle.LRUCache(C, E, n_layers=NL)
     main, side = torch.cuda.current_stream(), torch.cuda.Stream()
     xf = oracle.act_f64(x, wl.act_dtype)
     worst, n_host, n_fill = 0.0, 0, 0
-    C = wl.C
     for s in range(n_steps):
         if resizes and s in resizes:
             newC = resizes[s]
@@ -100,40 +117,44 @@ def _run_pipeline(B, name, Bt, n_steps, resizes=None):
             B.moe_move_slots(L.ctx, r, main)
             if newC < C:
                 slots[newC * nb:C * nb].fill_(0xFF)          # freed slots: any later read shows up as NaN
-            B.moe_bind_pools(L.ctx, slots, newC, host_pool, E)
+            B.moe_bind_pools(L.ctx, slots, newC, host_pool, NL * E)
             C = newC
-        L.route(d_logits[s * Bt:(s + 1) * Bt], Bt, main)
-        ids = L.ids[: Bt * k].cpu().numpy().reshape(Bt, k)          # synchronises the route
-        gates = L.w[: Bt * k].cpu().numpy().reshape(Bt, k)
-        rids, _ = oracle.route(logits[s], k)
-        assert np.array_equal(ids, rids), f"step {s}: routing"
-        B.moe_lru_step(L.ctx, 0, ids, Bt, plan)
-        want = ref_cache.step(ids, 52.7, 77.3)
-        for f in ("hit", "hit_slot", "fill", "fill_slot", "fill_victim", "host"):
-            assert plan.get(f).tolist() == list(want[f]), f"step {s}: plan field {f}"
-        B.moe_fill(L.ctx, plan, side)
-        hits, hsl = plan.get("hit").copy(), plan.get("hit_slot").copy()
-        fills, fsl = plan.get("fill").copy(), plan.get("fill_slot").copy()
-        L.ffn(d_x[s * Bt:(s + 1) * Bt], Bt, slots, hits, hsl, shared, ws, main, h_ids=ids)
-        B.moe_fill_wait(L.ctx, main)
-        L.ffn(d_x[s * Bt:(s + 1) * Bt], Bt, slots, fills, fsl, None, 0, main, h_ids=ids)
-        host = plan.c.n_host > 0
-        if host:
-            h_x.copy_(d_x[s * Bt:(s + 1) * Bt].reshape(-1))
-            B.moe_host_ffn(L.ctx, h_x, Bt, ids, np.ascontiguousarray(gates), plan, h_y, 8)
-            d_y.copy_(h_y)
-        gpu = np.concatenate([hits, fills]).astype(np.int32)
-        L.merge(gpu, ws, d_y if host else None, Bt, out, main)
-        y = out_f64(out, wl, Bt)
-        ref = oracle.moe_layer(xf[s * Bt:(s + 1) * Bt], ids, gates.astype(np.float64), ex,
-                               shared=ex.f64(E) if ws else None)
-        err = rel_err_rows(y, ref).max()
-        assert np.isfinite(y).all() and err <= TOL[wl.wdtype], f"step {s}: rel err {err}"
-        worst = max(worst, err)
-        n_host += len(want["host"])
-        n_fill += len(want["fill"])
+        for l in range(NL):
+            ex = exs[l][0]
+            L.route(d_logits[l][s * Bt:(s + 1) * Bt], Bt, main)
+            ids = L.ids[: Bt * k].cpu().numpy().reshape(Bt, k)          # synchronises the route
+            gates = L.w[: Bt * k].cpu().numpy().reshape(Bt, k)
+            rids, rgates = routes[l][s]
+            assert np.array_equal(ids, rids), f"step {s} layer {l}: routing"
+            assert np.abs(gates - rgates).max() <= 1e-6 * np.abs(rgates).max(), f"step {s} layer {l}: gates"
+            B.moe_lru_step(L.ctx, l, ids, Bt, plan)
+            want = ref_cache.step(rids, 52.7, 77.3, layer=l)
+            for f in ("hit", "hit_slot", "fill", "fill_slot", "fill_victim", "host"):
+                assert plan.get(f).tolist() == list(want[f]), f"step {s} layer {l}: plan field {f}"
+            B.moe_fill(L.ctx, plan, side)
+            hits, hsl = plan.get("hit").copy(), plan.get("hit_slot").copy()
+            fills, fsl = plan.get("fill").copy(), plan.get("fill_slot").copy()
+            sh = shared[l] if ws else None
+            L.ffn(d_x[s * Bt:(s + 1) * Bt], Bt, slots, hits, hsl, sh, ws, main, h_ids=ids)
+            B.moe_fill_wait(L.ctx, main)
+            L.ffn(d_x[s * Bt:(s + 1) * Bt], Bt, slots, fills, fsl, None, 0, main, h_ids=ids)
+            host = plan.c.n_host > 0
+            if host:
+                h_x.copy_(d_x[s * Bt:(s + 1) * Bt].reshape(-1))
+                B.moe_host_ffn(L.ctx, h_x, Bt, ids, np.ascontiguousarray(gates), plan, h_y, 8)
+                d_y.copy_(h_y)
+            gpu = np.concatenate([hits, fills]).astype(np.int32)
+            L.merge(gpu, ws, d_y if host else None, Bt, out, main)
+            y = out_f64(out, wl, Bt)
+            ref = oracle.moe_layer(xf[s * Bt:(s + 1) * Bt], rids, rgates, ex, shared=ex.f64(E) if ws else None)
+            err = rel_err_rows(y, ref).max()
+            assert np.isfinite(y).all() and err <= TOL[wl.wdtype], f"step {s} layer {l}: rel err {err}"
+            worst = max(worst, err)
+            n_host += len(want["host"])
+            n_fill += len(want["fill"])
     print(f"[pipeline] {name}: worst rel err {worst:.2e}, fills {n_fill}, host experts {n_host}", flush=True)
-    assert np.array_equal(B.moe_lru_slots(L.ctx, 0, E), ref_cache.slot_table(0))
+    for l in range(NL):
+        assert np.array_equal(B.moe_lru_slots(L.ctx, l, E), ref_cache.slot_table(l))
     assert n_fill > 0
     L.close()
 
@@ -151,8 +172,12 @@ def _stream_workload(case):
 
 
 @pytest.mark.parametrize("case,T,n_layers", [("f32_gemv", 16, 3), ("bf16_gemm", 64, 3), ("mxfp4_shared", 48, 2),
-                                             ("a3b_layer", 40, 2)])
+                                             ("a3b_layer", 40, 2), ("a3b_layer", 8192, 2)])
 def test_prefill_stream(B, case, T, n_layers):
+    """A chunk streamed through n_layers layers (double- and single-buffered) is bit-identical
+    to each layer run with its pool resident, and matches the oracle on sampled tokens.  The
+    8192-token case streams two full a3b layer pools (1.2 GB each) through the same path the
+    bench times."""
     from expert_cached_moe_amd.runtime import LayerBuffers, pack_pool
     print(f"[stream] {case} T={T} layers={n_layers}", flush=True)
     wl = _stream_workload(case)
@@ -198,8 +223,10 @@ def test_prefill_stream(B, case, T, n_layers):
         got = outs[2][l * T * H:(l + 1) * T * H]
         assert torch.equal(got, res), f"layer {l}: streamed output differs from the resident layer"
         ids = Lb.ids[: T * wl.k].cpu().numpy().reshape(T, wl.k)
-        assert np.array_equal(ids, oracle.route(logits[l], wl.k)[0])
-        g = Lb.w[: T * wl.k].cpu().numpy().reshape(T, wl.k).astype(np.float64)
+        rids, g = oracle.route(logits[l], wl.k)
+        assert np.array_equal(ids, rids)
+        gw = Lb.w[: T * wl.k].cpu().numpy().reshape(T, wl.k)
+        assert np.abs(gw - g).max() <= 1e-6 * np.abs(g).max()
         f64 = {}
 
         def expert(e, l=l, f64=f64):
@@ -207,7 +234,7 @@ def test_prefill_stream(B, case, T, n_layers):
                 f64[e] = oracle.expert_f64(exs[l][e], wl.wdtype)
             return f64[e]
 
-        ref = oracle.moe_layer(xf[sample], ids[sample], g[sample], expert, shared=expert(E) if ws else None)
+        ref = oracle.moe_layer(xf[sample], rids[sample], g[sample], expert, shared=expert(E) if ws else None)
         err = rel_err_rows(out_f64(got, wl, T)[sample], ref).max()
         assert err <= TOL[wl.wdtype], f"layer {l}: rel err {err}"
         del pool_l

@@ -38,6 +38,34 @@ def test_route_tie_fixture():
         assert ids[0].tolist() == [int(v) for v in want.split()], ln
 
 
+def _router_cases():
+    cases, cur = [], None
+    for ln in _lines("router_logits.txt"):
+        tag, *vals = ln.split()
+        if tag == "case":
+            cur = {"name": vals[0], "x": [], "wr": [], "l": []}
+        elif tag == "end":
+            cases.append(cur)
+        else:
+            cur[tag].append([float.fromhex(v) if "0x" in v else float(v) for v in vals])
+    return cases
+
+
+def test_router_logits_fixture():
+    """Hand-worked logits, bit for bit: a scaled, transposed or partly dropped product fails
+    the first case; accumulating in fp32 (instead of one rounding of the exact sum) fails the
+    other two."""
+    cases = _router_cases()
+    assert len(cases) == 3
+    for c in cases:
+        x = np.array(c["x"], np.float32)
+        wr = np.array(c["wr"], np.float32)
+        want = np.array(c["l"], np.float32)
+        got = oracle.router_logits(x, wr)
+        assert got.dtype == np.float32 and got.shape == want.shape, c["name"]
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (c["name"], got, want)
+
+
 def _dominance_topk(row, k):
     """Brute force: the unique ordered k-list whose members beat every non-member."""
     E = len(row)
