@@ -36,6 +36,7 @@ EXPORTS = [
     "moe_fill", "moe_fill_wait", "moe_upload", "moe_expert_ffn", "moe_host_ffn", "moe_merge_partial",
     "moe_expert_ffn_merge",
     "moe_prefill_stream", "moe_router_logits", "moe_lru_resize", "moe_move_slots",
+    "moe_expert_ffn_merge_noalloc", "moe_noalloc_scratch_bytes",
 ]
 
 
@@ -97,6 +98,9 @@ _sig = {
                                          ctypes.c_int32, vp, vp]),
     "moe_expert_ffn_merge": (ctypes.c_int, [vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp,
                                             ctypes.c_int32, vp, vp, vp, vp]),
+    "moe_expert_ffn_merge_noalloc": (ctypes.c_int, [vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
+                                                    vp, ctypes.c_int32, vp, vp, vp]),
+    "moe_noalloc_scratch_bytes": (ctypes.c_int64, []),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -334,6 +338,22 @@ def moe_expert_ffn_merge(ctx, d_x, T, h_topk_ids, d_topk_ids, d_topk_w, d_slot_b
     _check(ctx, _lib.moe_expert_ffn_merge(ctx, _ptr(d_x), T, _ptr(hi), _ptr(d_topk_ids), _ptr(d_topk_w),
                                           _ptr(d_slot_base), _ptr(he), _ptr(hs), n, _ptr(d_shared), with_shared,
                                           _ptr(d_y_host), _ptr(d_out), _ptr(d_ws), _stream(s)))
+
+
+def moe_expert_ffn_merge_noalloc(ctx, d_x, T, h_topk_ids, d_topk_ids, d_topk_w, d_slot_base, h_experts, h_slots, n,
+                                 d_shared, with_shared, d_y_host, d_out, s=None) -> None:
+    he = np.ascontiguousarray(h_experts, dtype=np.int32) if h_experts is not None else None
+    hs = np.ascontiguousarray(h_slots, dtype=np.int32) if h_slots is not None else None
+    hi = h_topk_ids
+    if isinstance(hi, np.ndarray):
+        hi = np.ascontiguousarray(hi, dtype=np.int32)
+    _check(ctx, _lib.moe_expert_ffn_merge_noalloc(ctx, _ptr(d_x), T, _ptr(hi), _ptr(d_topk_ids), _ptr(d_topk_w),
+                                                  _ptr(d_slot_base), _ptr(he), _ptr(hs), n, _ptr(d_shared),
+                                                  with_shared, _ptr(d_y_host), _ptr(d_out), _stream(s)))
+
+
+def moe_noalloc_scratch_bytes() -> int:
+    return int(_lib.moe_noalloc_scratch_bytes())
 
 
 def moe_prefill_stream(ctx, d_layer_bufs, n_buffers, d_logits, d_x, T, d_shared, d_topk_ids, d_topk_w, d_counts,

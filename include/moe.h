@@ -304,6 +304,23 @@ int moe_expert_ffn_merge(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t
                          const int32_t* h_experts, const int32_t* h_slots, int32_t n, const void* d_shared,
                          int32_t with_shared, const float* d_y_host, void* d_out, void* d_ws, hipStream_t s);
 
+/* moe_expert_ffn_merge without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the scratch lives in one file-scope device array of moe_noalloc_scratch_bytes() bytes
+ * (8 MiB) that each GPU the library runs on holds until the process ends.  Same arguments,
+ * results (bit for bit) and errors as moe_expert_ffn_merge, without d_ws; the call makes no
+ * device allocation and needs no initialised scratch.  Every call on one GPU uses that GPU's
+ * array (it keeps the last call's contents), so calls that overlap on one GPU (other streams,
+ * other threads or contexts) race: order them.  A batch whose workspace
+ * (moe_workspace_bytes(cfg, T)) exceeds the array is refused with MOE_ECAPACITY before any
+ * GPU work; MOE_EHIP if the array's device address cannot be obtained. */
+int moe_expert_ffn_merge_noalloc(moe_ctx* ctx, const void* d_x, int32_t T, const int32_t* h_topk_ids,
+                                 const int32_t* d_topk_ids, const float* d_topk_w, const void* d_slot_base,
+                                 const int32_t* h_experts, const int32_t* h_slots, int32_t n, const void* d_shared,
+                                 int32_t with_shared, const float* d_y_host, void* d_out, hipStream_t s);
+/* Bytes of the scratch array moe_expert_ffn_merge_noalloc uses on each GPU. */
+int64_t moe_noalloc_scratch_bytes(void);
+
 /* ---------------------------------------------------------------- layer streaming (prefill) */
 /* One T-token prefill chunk through cfg.n_layers MoE layers whose expert pools
  * stream from the bound host pool (n_layers*E blobs, layer-major, pinned) into

@@ -371,3 +371,19 @@ def test_ffn_merge_argument_errors():
     assert status(h_topk_ids=np.array([[0, 1, 2, 3, 4, 5, 6, 6]], np.int32)) == B.MOE_EINVAL
     assert status(with_shared=1, d_shared=64) == B.MOE_EINVAL
     B.moe_destroy(ctx)
+
+
+def test_noalloc_rejects_oversized_batch():
+    """moe_expert_ffn_merge_noalloc refuses a decode batch whose scratch exceeds the library's
+    array (MXFP4, hidden = inter = 16384, 512 experts top-16 + shared: 8.9 MB at T = 8) before
+    any GPU work; the same layer at T = 7 fits.  (The addresses are never dereferenced.)"""
+    cfg = B.make_config(16384, 16384, 512, 16, 1, 0, 1, B.MOE_W_MXFP4)
+    assert B.moe_workspace_bytes(cfg, 8) > B.moe_noalloc_scratch_bytes() >= B.moe_workspace_bytes(cfg, 7)
+    ctx = B.moe_create(cfg)
+    ids = np.arange(8 * 16, dtype=np.int32).reshape(8, 16)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_expert_ffn_merge_noalloc(ctx, 256, 8, ids, 256, 256, 256, np.arange(128), np.arange(128), 128, 256, 1,
+                                       None, 256, None)
+    assert ei.value.status == B.MOE_ECAPACITY
+    assert "exceeds" in B.moe_last_error(ctx)
+    B.moe_destroy(ctx)
