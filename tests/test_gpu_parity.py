@@ -332,13 +332,14 @@ def test_prefill_mxfp4_register_staged(B, H, I):
     G.L.close()
 
 
-@pytest.mark.parametrize("name,n_sample", [("a3b_prefill8k_bf16", 24), ("v4flash_mxfp4", 8)])
-def test_prefill_full_size_sampled(B, name, n_sample):
-    """8192-token prefill chunk at full size through the grouped GEMM; the oracle checks a
-    sample of tokens (first, last and random ones) one by one."""
-    print(f"[prefill-full] {name}", flush=True)
+@pytest.mark.parametrize("name,n_sample,T", [("a3b_prefill8k_bf16", 24, 8192), ("v4flash_mxfp4", 8, 8192),
+                                            ("a3b_prefill8k_bf16", 12, 16384)])
+def test_prefill_full_size_sampled(B, name, n_sample, T):
+    """Prefill chunks at full size (8192 tokens, and the 16384-token chunk of the streamed
+    ablation) through the grouped GEMM; the oracle checks a sample of tokens (first, last and
+    random ones) one by one."""
+    print(f"[prefill-full] {name} T={T}", flush=True)
     wl = synth.workload(name)
-    T = wl.T
     ex = Experts(wl)
     logits = synth.iid_logits(wl, T)
     G = GpuLayer(B, wl, list(range(wl.E)), T, ex=ex)
