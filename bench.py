@@ -413,13 +413,16 @@ def decode(args, wl, Bt, experts):
               shared[r] if shared else None, with_shared, st, h_ids=h_ids_steps[t])
         L.merge(step_experts[t], with_shared, None, Bt, out, st)
 
-    def graph_ms(body, n, n_rep=NR):
-        """Capture body(W + s) for s < n; per-iteration ms of each timed replay."""
+    def graph_ms(body, n, n_rep=NR, name="graph"):
+        """Capture body(W + s) for s < n; per-iteration ms of each timed replay.  The replays run
+        inside a marker range of their own (``name``), so a kernel trace taken with
+        --marker-trace attributes every dispatch to the graph it belongs to."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for s in range(n):
                 body(W + s)
-        ts = timed_replays(g, stream, n_rep)
+        with _phase(f"{wl.name} b{Bt} {name}"):
+            ts = timed_replays(g, stream, n_rep)
         del g
         return [t / n for t in ts]
 
@@ -427,10 +430,10 @@ def decode(args, wl, Bt, experts):
         for s in range(min(W, 64)):                        # eager warm-up (code objects, caches)
             enqueue(s)
     torch.cuda.synchronize()
-    step_ms = graph_ms(enqueue, K)
+    step_ms = graph_ms(enqueue, K, name="step")
     ms_per_step = float(np.median(step_ms))
     value = Bt / (ms_per_step / 1e3)
-    two_calls_ms = float(np.median(graph_ms(enqueue_two_calls, K)))
+    two_calls_ms = float(np.median(graph_ms(enqueue_two_calls, K, name="two-call step")))
 
 
     # ---------------------------------------------------------------- decode FFN roofline
@@ -438,9 +441,10 @@ def decode(args, wl, Bt, experts):
     # steps alone in one graph: each call reads its experts from the next pool replica, so the
     # weights come from HBM, and the per-call time is the two kernels' durations back to back.
     n_prof = max(K, 100)
-    ffn_ms = float(np.median(graph_ms(ffn, n_prof)))
-    warm_ms = float(np.median(graph_ms(lambda s_idx: ffn(s_idx, rotate=False), n_prof, 3)))
-    fused_ms = float(np.median(graph_ms(lambda s_idx: ffn_merge(s_idx, step_experts, step_slots), n_prof)))
+    ffn_ms = float(np.median(graph_ms(ffn, n_prof, name="ffn roofline")))
+    warm_ms = float(np.median(graph_ms(lambda s_idx: ffn(s_idx, rotate=False), n_prof, 3, name="ffn warm")))
+    fused_ms = float(np.median(graph_ms(lambda s_idx: ffn_merge(s_idx, step_experts, step_slots), n_prof,
+                                        name="ffn+merge call")))
     pairs = Bt * k + (Bt if with_shared else 0)
     act = 2 if wl.act_dtype == "bf16" else 4
     w_bytes = 0.0
@@ -477,7 +481,7 @@ def decode(args, wl, Bt, experts):
         cfg_c = B.make_config(wl.H, wl.I, E, k, wl.n_shared, wl.C, 1, dt, 1, 0, 52.7, 77.3)
         ce, cs, cnd, cst = plan_sets(cfg_c)
         gpu_share = float(np.sum([len(e) for e in ce]) / max(1, np.sum(cnd)))
-        c_ms = float(np.median(graph_ms(lambda s_idx: enqueue(s_idx, ce, cs), K)))
+        c_ms = float(np.median(graph_ms(lambda s_idx: enqueue(s_idx, ce, cs), K, name="cache-limited step")))
         cache_limited = {"slots": wl.C, "bp_bh": [52.7, 77.3], "tokens_per_s": round(Bt / (c_ms / 1e3), 1),
                          "ms_per_step": round(c_ms, 5),
                          "gpu_experts_per_step": round(float(np.mean([len(e) for e in ce])), 3),
@@ -543,12 +547,13 @@ def prefill(args, name):
     with torch.cuda.graph(g, stream=stream):
         for _ in range(args.prefill_reps):
             step()
-    chunk_ms = [t / args.prefill_reps for t in timed_replays(g, stream, 5)]
+    with _phase(f"prefill {name} chunk graph"):
+        chunk_ms = [t / args.prefill_reps for t in timed_replays(g, stream, 5)]
     ms = float(np.median(chunk_ms))
     del g
     # FFN alone (events around the grouped GEMMs of eager chunks)
     gemm_ms = []
-    with torch.cuda.stream(stream):
+    with _phase(f"prefill {name} gemm timing"), torch.cuda.stream(stream):
         for _ in range(7):
             step(events=True)
             torch.cuda.synchronize()

@@ -509,8 +509,13 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_decode_down_merge(const De
     }
 }
 
+// Lanes per down row (LPR) and 16-byte chunks per lane (CPL) with LPR * CPL = chunks per row.
+// At most 32 lanes a row where the row allows it: the fused down + merge kernel then covers at
+// least 4 rows per workgroup (v4flash bf16, 192 chunks a row, batch 1: 1 us off the 52 us step
+// against 64 lanes with separate down and merge kernels), and the separate down kernel uses
+// the same lanes and chunks, so both give the same bits (0.3% slower at batch 8 than 64 lanes).
 bool pick_down(int d_ch, int* lpr, int* cpl) {
-    for (int l : {64, 32, 16})
+    for (int l : {32, 16, 64})
         for (int c : {1, 2, 3, 4, 6, 8})
             if (l * c == d_ch) { *lpr = l; *cpl = c; return true; }
     return false;
@@ -667,10 +672,11 @@ hipError_t launch_ffn_decode_merge(const moe_config& c, const BlobLayout& lay, c
                                    const int32_t* ids, const float* w, const uint32_t* mask, int32_t with_shared,
                                    const float* y_host, void* out, void* ws, hipStream_t s) {
     // The fused kernel when every wave takes one entry and a workgroup covers at least 4
-    // output rows (at most 32 lanes per down row).  Measured on MI355X: with more entries a
-    // wave takes several experts one after another, and with 2 rows per workgroup (64 lanes
-    // per row) the per-workgroup merge outweighs the saved launch; both run slower fused
-    // than the separate down and merge kernels (pair outputs in the workspace).
+    // output rows (at most 32 lanes per down row; rows of 192 chunks, bf16 with I = 1536, run
+    // 32 lanes of 6 chunks).  Measured on MI355X: with more entries a wave takes several
+    // experts one after another, and with 2 rows per workgroup (64 lanes per row) the
+    // per-workgroup merge outweighs the saved launch; both run slower fused than the separate
+    // down and merge kernels (pair outputs in the workspace).
     // no listed expert has a token (and no shared expert): the output is the host part, or zero
     if (list.n == 0) return launch_merge(c, nullptr, ids, w, mask, 0, y_host, T, out, s);
     int lpr = 64, cpl = 0;

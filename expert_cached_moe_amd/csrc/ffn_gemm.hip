@@ -684,7 +684,7 @@ template <bool FP4> struct Lay {
     static constexpr int EPI = STAGE;
     static constexpr int ROWTAB = EPI + BM * HSTR;        // output row of each tile row (GEMM 2)
     static constexpr int SCALES = ROWTAB + BM * 4;
-    static constexpr int kLdsBytes = FP4 ? SCALES + BM * kMaxKFp4 / 32 : ROWTAB + BM * 4;
+    static constexpr int kLdsBytes = FP4 ? SCALES + BM * (kMaxKFp4 / 32 + 16) : ROWTAB + BM * 4;
     static_assert(kLdsBytes <= 160 * 1024 && ROWTAB >= 2 * STAGE, "LDS per CU; the row table is outside the stages");
     static_assert(QB * NW * 1024 == BN * BROWB && QB >= 1, "weight loads split over the waves");
 };
@@ -788,13 +788,32 @@ __device__ __forceinline__ void issue(uint8_t* lds8, const uint8_t* a_src, const
     }
 }
 
-// MXFP4: the tile's scales (BM rows x K/32 bytes, contiguous in the blob) into LDS.
+// MXFP4: LDS row stride of the tile's scales.  The 32 lanes of a fragment read one scale byte
+// each from 32 consecutive rows; rows of an even number of 16-byte chunks (K/32 = 64 or 128
+// bytes) would put those bytes in 2 or 4 banks, so such rows get one 16-byte pad chunk, which
+// spreads them over 16 banks.  Rows that are not whole chunks (K not a multiple of 512) are
+// copied back to back.
+__device__ __forceinline__ int scale_stride(int K) {
+    const int rb = K / 32;
+    return rb % 16 == 0 && (rb / 16) % 2 == 0 ? rb + 16 : rb;
+}
+
+// MXFP4: the tile's scales (BM rows x K/32 bytes, contiguous in the blob) into LDS, rows
+// scale_stride(K) bytes apart (the pad chunk of a row repeats its last chunk; never read).
 __device__ __forceinline__ void issue_scales(uint8_t* lds8, const uint8_t* sbase, int K) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int chunks = BM * (K / 32) / 16;               // a multiple of 64 (K a multiple of 128)
+    const int rb = K / 32, stride = scale_stride(K);
+    const int chunks = BM * stride / 16;                 // a multiple of 64 (K a multiple of 128)
     uint8_t* dst = lds8 + Lay<true>::SCALES;
-    for (int c0 = wave * 64; c0 < chunks; c0 += kThreads)
-        __builtin_amdgcn_global_load_lds(sbase + (c0 + lane) * 16, dst + c0 * 16, 16, 0, 0);
+    for (int c0 = wave * 64; c0 < chunks; c0 += kThreads) {
+        const int c = c0 + lane;
+        int src = c * 16;                                // rows back to back
+        if (stride != rb) {
+            const int cpr = stride / 16, r = c / cpr, j = c - r * cpr;
+            src = r * rb + min(j, rb / 16 - 1) * 16;
+        }
+        __builtin_amdgcn_global_load_lds(sbase + src, dst + c0 * 16, 16, 0, 0);
+    }
 }
 
 // 8 MXFP4 codes (low nibble first) times the block scale, as bf16 MFMA operands
@@ -855,7 +874,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
                 for (int j = 0; j < big::FN; ++j) {
                     const int R = wn * big::TN + j * 32 + lane % 32;
                     bq[j] = *reinterpret_cast<const uint4*>(bs_ + R * 32 + (big::swz4(R, lane / 32) << 4));
-                    const uint32_t sc = lds8[L::SCALES + R * (a.K / 32) + ks * 2 + lane / 32];
+                    const uint32_t sc = lds8[L::SCALES + R * big::scale_stride(a.K) + ks * 2 + lane / 32];
                     bsc[j] = sc ? __uint_as_float(sc << 23) : __uint_as_float(0x00400000u);
                 }
             }

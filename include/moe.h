@@ -291,7 +291,7 @@ int moe_merge_partial(moe_ctx* ctx, const void* d_o, const int32_t* d_topk_ids, 
  * (h_experts doubles as h_gpu_experts), bit for bit, without the pair outputs going
  * through memory when the call lists at most 8 entries (routed experts + the shared
  * one), k <= 8 and the decode kernel reads a down-projection row with at most 32 lanes
- * (bf16 with I = 768 and MXFP4 with I = 1536 do; bf16 with I = 1536 does not): the down
+ * (the workloads' shapes do: bf16 with I = 768 or 1536, MXFP4 with I = 1536): the down
  * projection and the gate-weighted merge then share one kernel; otherwise the separate
  * kernels run with the pair outputs in d_ws.
  * Decode batches only: T <= 8, h_topk_ids given, and the shapes of the decode kernels
