@@ -98,14 +98,19 @@ def payload_bytes(wl):
 
 
 # HBM traffic of the decode FFN kernels from hardware counters (rocprofv3 --pmc FETCH_SIZE, then
-# --pmc WRITE_SIZE, over the command in profiles/decode_ffn_hbm_traffic.md), in KiB per dispatch
+# --pmc WRITE_SIZE, over the commands in profiles/decode_ffn_and_prefill_gemm_hbm_traffic.md), in KiB per dispatch
 # as the counters read them, averaged over the calls of the rotating FFN graph and summed over
 # k_decode_gate_up and k_decode_down of one moe_expert_ffn call at batch 1 (every call has the
 # same expert count, so the record matches the timed calls).  The same runs read the plain
 # 256 MiB read + 256 MiB write kernel of --copy-probe, whose readings give the scale factors.
 # A record applies only while the decode kernel sources hash to the value it was taken with.
 DECODE_SOURCES = ("ffn_decode.hip", "ffn_common.h", "device_common.h")
-TRAFFIC = {}
+_SRC = "c82e60e3d3c4f777211e85ae21fd14b1173474931bd8b948d1885c2eae4b6dfd"
+TRAFFIC = {
+    ("v4flash_decode_bf16", 1): {"sha256": _SRC, "fetch_kib": 86070.0 + 43120.0, "write_kib": 84.0 + 56.0},
+    ("a3b_decode_bf16", 1): {"sha256": _SRC, "fetch_kib": 24610.0 + 12360.0, "write_kib": 48.0 + 32.0},
+    ("v4flash_mxfp4", 1): {"sha256": _SRC, "fetch_kib": 22920.0 + 11550.0, "write_kib": 42.0 + 56.0},
+}
 FETCH_FACTOR = 262144.0 / 131080.0
 WRITE_FACTOR = 1.0
 
