@@ -204,7 +204,7 @@ __global__ void __launch_bounds__(64 * kGateUpWaves) k_decode_gate_up(const Deco
         }
         // after the halving reduction lanes l and l^32 hold (gate, up) of one column
         const int qi = dev::group_reduce_split<RPW, 64>(part, lane);
-        const float up = __shfl_xor(part[0], 32, kWave);
+        const float up = dev::other_half(part[0]);
         if ((lane & 32) == 0 && (lane & (64 / RPW - 1)) == 0)
             store_act<WT>(a.out, int64_t(p) * a.I + col0 + qi, silu(part[0]) * up);
     };
