@@ -5,10 +5,11 @@
 // streams 16-byte chunks of weight rows into registers (consecutive lanes read
 // consecutive chunks: 1 KiB per wave load instruction); the tokens routed to the
 // expert are applied to the registers and each row sum is reduced across the lanes
-// of the row with a halving shuffle exchange.  For bf16 and fp32 weights every wave is
-// independent (no LDS, no barrier); MXFP4 copies the activation rows into LDS once per
-// workgroup (one barrier per group of rows), and the fused down + merge kernel keeps its
-// pair outputs in LDS.  Which tokens use which expert comes from the host's copy of the
+// of the row with a halving exchange (DPP moves and permlane swaps).  The gate/up kernel
+// copies the activation rows (x) into LDS once per workgroup for bf16 and MXFP4 weights (one
+// barrier per group of rows), as does the MXFP4 down kernel for h; the fp32 kernels and the
+// bf16 down kernel read them straight from memory with independent waves, and the fused
+// down + merge kernel keeps its pair outputs in LDS.  Which tokens use which expert comes from the host's copy of the
 // step's top-k ids (the host needs them anyway to plan the cache), packed into the
 // kernel arguments, so these kernels do not wait for the router kernel.
 //
@@ -68,7 +69,9 @@ struct DecodeArgs {
 // MXFP4 decode FFN).  The copies are issued after the weight loads: fetching the
 // activations first and letting the products start as each weight chunk lands
 // (per-chunk waits) measured 15-20% slower than streaming the weights at once and
-// waiting for everything.
+// waiting for everything.  bf16 activations take the same path with the row copied as is:
+// one copy per workgroup instead of one global read per wave (decode FFN at batch 8: 1-2%
+// faster on MI355X).
 __device__ __forceinline__ void barrier_loads() {
     __builtin_amdgcn_s_waitcnt(0);      // vmcnt(0) expcnt(0) lgkmcnt(0): own LDS-bound loads landed
     __syncthreads();
@@ -84,6 +87,18 @@ __device__ __forceinline__ void stage_row(uint4* xs, const uint8_t* act, int row
         const int S = u * kWave + lane, i = S / cpr, j = S - i * cpr;
         __builtin_amdgcn_global_load_lds(src + 64 * j + 16 * i, xs + slot * units + u * kWave, 16, 0, 0);
     }
+}
+
+// bf16: row `row` copied as is (chunk j at 16-byte slot j of the row's staging slot)
+__device__ __forceinline__ void stage_row_plain(uint4* xs, const uint8_t* act, int row, int K, int slot, int wave, int nw,
+                                                int lane) {
+    const int units = K / 8;
+    const uint8_t* src = act + int64_t(row) * K * 2;
+    for (int u = wave; u * kWave < units; u += nw)
+        __builtin_amdgcn_global_load_lds(src + 16 * (u * kWave + lane), xs + slot * units + u * kWave, 16, 0, 0);
+}
+__device__ __forceinline__ void read_staged(ActChunk<WT_BF16>& av, const uint4* xs, int K, int slot, int chunk) {
+    av.v[0] = xs[slot * (K / 8) + chunk];
 }
 
 __device__ __forceinline__ void read_staged(ActChunk<WT_FP4>& av, const uint4* xs, int K, int slot, int chunk) {
@@ -209,7 +224,7 @@ __global__ void __launch_bounds__(64 * kGateUpWaves) k_decode_gate_up(const Deco
             store_act<WT>(a.out, int64_t(p) * a.I + col0 + qi, silu(part[0]) * up);
     };
     int p, t;
-    if constexpr (WT != WT_FP4) {
+    if constexpr (WT == WT_F32) {
         while (it.next(p, t))
             token(p, [&](ActChunk<WT>& av, int c) {
                 load_act<WT>(av, a.act + (int64_t(t) * a.H + int64_t(c * kWave + lane) * EPC) * AB);
@@ -224,7 +239,8 @@ __global__ void __launch_bounds__(64 * kGateUpWaves) k_decode_gate_up(const Deco
         auto stage_group = [&](TokenIter g, int gp, int gt) {
             int n = 0;
             for (bool gh = true; n < a.nt && gh; ++n) {
-                stage_row(xs, a.act, gt, a.H, n, wave, WPB, lane);
+                if constexpr (WT == WT_FP4) stage_row(xs, a.act, gt, a.H, n, wave, WPB, lane);
+                else stage_row_plain(xs, a.act, gt, a.H, n, wave, WPB, lane);
                 gh = g.next(gp, gt);
             }
             return n;
@@ -526,7 +542,7 @@ hipError_t launch_gu1(const DecodeArgs& a, int n_list, hipStream_t s) {
     using S = GateUpShape<CPL>;
     if (a.I % S::COLS) return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_decode_gate_up<WT, CPL>), dim3(a.I / S::COLS, n_list), dim3(64 * S::WPB),
-                       WT == WT_FP4 ? a.nt * a.H * 2 : 0, s, a);
+                       WT != WT_F32 ? a.nt * a.H * 2 : 0, s, a);
     return hipGetLastError();
 }
 

@@ -721,15 +721,25 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& a, int lid, int n_tile
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave / WN;
     Tile t;
-    const int slot = lid / n_tiles, nt = lid % n_tiles;
+    const int slot = lid / n_tiles;
+    int nt = lid % n_tiles;
     const int tinfo = a.tiles[1 + slot];
-    const int ei = tinfo >> 16, mt = tinfo & 0xFFFF;
+    const int ei = tinfo >> 16;
+    int mt = tinfo & 0xFFFF;
     const int entry = a.list.ent[ei];
     const int e = entry & 1023;
     const bool shared = e == kSharedTag;
     const uint8_t* blob = shared ? a.shared_blob : a.slot_base + int64_t(entry >> 10) * a.blob_bytes;
     const int base = shared ? 0 : a.offsets[e];
     t.rows = shared ? a.T : a.offsets[e + 1] - base;
+    {
+        // inside an expert the m-tiles run fastest: the tiles that share a weight block are
+        // adjacent, so they run at the same time on one XCD (a3b 8K chunk: GEMMs 3% faster)
+        const int mte = (t.rows + BM - 1) / BM;
+        const int off = lid - n_tiles * (slot - mt);   // the expert's tiles start at slot - mt
+        nt = off / mte;
+        mt = off % mte;
+    }
     t.m0 = mt * BM;
     t.n0 = nt * BN;
     const int fa = (t.rows - t.m0 - wm * TM + 31) / 32;   // fragment rows of this wave that hold rows
