@@ -332,6 +332,29 @@ def test_prefill_mxfp4_register_staged(B, H, I):
     G.L.close()
 
 
+def test_prefill_bf16_large_tile_down(B):
+    """bf16 prefill with an intermediate size of 2048: the down GEMM (K = I = 2048) runs the
+    large-tile kernel (the workloads' bf16 down GEMMs have K = 768 and run the pipelined one),
+    the gate/up GEMM (K = H = 1024) the pipelined kernel.  Ragged 40-token batch with a shared
+    expert, so tiles end part way and the pair-output rows come from the row table."""
+    print("[prefill-bf16-big-down] H=1024 I=2048", flush=True)
+    base = synth.workload("v4flash_decode_bf16")
+    wl = dataclasses.replace(base, name="bf16_1024x2048", H=1024, I=2048, E=8, k=2, C=8, T=40)
+    T = wl.T
+    logits = synth.iid_logits(wl, T, tag=T + 7)
+    present = sorted(set(oracle.route(logits, wl.k)[0].ravel().tolist()))
+    G = GpuLayer(B, wl, present, T)
+    x = synth.activations(wl, T, tag=T + 7)
+    out = G.run(logits, x, present, 1)
+    ids, gates = check_route(G, logits, T)
+    y = _out_f64(out, wl, T)
+    ref = oracle.moe_layer(oracle.act_f64(x, wl.act_dtype), ids, gates, G.ex, shared=G.ex.f64(wl.E))
+    err = rel_err_rows(y, ref)
+    assert err.max() <= TOL[wl.wdtype], err.max()
+    assert np.median(err) <= 6e-3, np.median(err)
+    G.L.close()
+
+
 @pytest.mark.parametrize("name,n_sample,T", [("a3b_prefill8k_bf16", 24, 8192), ("v4flash_mxfp4", 8, 8192),
                                             ("a3b_prefill8k_bf16", 12, 16384)])
 def test_prefill_full_size_sampled(B, name, n_sample, T):
