@@ -6,18 +6,23 @@
 // Pairs are grouped by expert (moe_route's stable permutation); per expert
 //   GEMM 1:  G = A_e . Wgu^T  (A_e = x rows of the expert's pairs, gathered)
 //            epilogue h = silu(gate) * up, stored as bf16 at the pair's sorted row;
-//   GEMM 2:  O = h_e . Wd^T, fp32, stored at the pair's row p = perm[pos].
-// bf16 inputs, fp32 accumulation on v_mfma_f32_16x16x32_bf16; MXFP4 weights are
-// dequantised to bf16 (exactly) while their tile is staged into LDS.
+//   GEMM 2:  O = h_e . Wd^T, accumulated in fp32 and stored as bf16 at the pair's row
+//            p = perm[pos] (the merge reads the pair outputs).
+// bf16 operands and fp32 accumulation on v_mfma_f32_32x32x16_bf16; MXFP4 weights are
+// decoded to bf16 operands (exactly) on their way from LDS to the MFMAs.
 //
-// Tiling: a workgroup computes a BM x BN output tile in K steps of 64; its waves
-// each own a block of MFMA tiles (16x16x32 or 32x32x16), fed from LDS rows padded by
-// 16 bytes, with the next step's global tiles prefetched into registers.  Gate and
-// up rows are interleaved in blocks of 16 in the weight layout, so the gate and up
-// values of a column meet in the same lane (16-wide tiles) or one lane exchange away
-// (32-wide tiles) and the SwiGLU epilogue stays in registers.  Tiles are numbered expert-major and each of the 8 XCDs
-// takes a contiguous range, so the A rows and weights of one expert are re-read
-// from that XCD's L2.
+// Three kernels, chosen per GEMM from N and K:
+//   k_gemm_big  persistent 256 x 256 tiles, K slices of 64 loaded straight into two LDS
+//               stages (bf16 GEMMs with K >= 2048, and every MXFP4 GEMM whose tile scales
+//               fit its LDS region);
+//   k_gemm_dma  128 x 256 tiles, a ring of 3 stages of K = 32 loaded straight into LDS, two
+//               workgroups per CU (the other bf16 GEMMs);
+//   k_gemm      register-staged tiles (MXFP4 shapes the large tile does not take).
+// Gate and up rows are interleaved in blocks of 16 in the weight layout, so the gate and up
+// values of a column are one lane exchange apart in a 32-wide fragment and the SwiGLU
+// epilogue needs no extra pass.  Tiles are numbered expert-major and each of the 8 XCDs takes
+// a contiguous range of the real tile count, so the A rows and weights of an expert are
+// re-read from that XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
