@@ -11,12 +11,14 @@
 // bf16 operands and fp32 accumulation on v_mfma_f32_32x32x16_bf16; MXFP4 weights are
 // decoded to bf16 operands (exactly) on their way from LDS to the MFMAs.
 //
-// Three kernels, chosen per GEMM from N and K:
+// Four kernels, chosen per GEMM from N and K:
 //   k_gemm_big  persistent 256 x 256 tiles, K slices of 64 loaded straight into two LDS
 //               stages (bf16 GEMMs with K >= 2048, and every MXFP4 GEMM whose tile scales
 //               fit its LDS region);
+//   k_gemm_b3   persistent 128 x 256 tiles, K slices of 64 in a ring of three LDS stages
+//               (the other bf16 GEMMs with at least three slices);
 //   k_gemm_dma  128 x 256 tiles, a ring of 3 stages of K = 32 loaded straight into LDS, two
-//               workgroups per CU (the other bf16 GEMMs);
+//               workgroups per CU (bf16 GEMMs with K = 64 or 128);
 //   k_gemm      register-staged tiles (MXFP4 shapes the large tile does not take).
 // Gate and up rows are interleaved in blocks of 16 in the weight layout, so the gate and up
 // values of a column are one lane exchange apart in a 32-wide fragment and the SwiGLU
@@ -1099,6 +1101,316 @@ k_gemm_big(const GemmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- three-stage bf16 GEMM
+// 128 x 256 tiles, K slices of 64 (whole 128-byte row segments) loaded straight into a ring
+// of three 48 KiB LDS stages, so the loads of a slice have two slices of MFMA time to land
+// (the 256 x 256 tile's 64 KiB stages leave room for two).  8 waves (2 x 4) of 64 x 64 = 2 x 2
+// fragments of 32x32x16 MFMA.  Persistent like the large tile: a workgroup walks its XCD's
+// share of the tiles, the stage ring continues across its tiles, and the next tile's first two
+// slices are loaded under the current tile's last slices; its third after the epilogue, which
+// is staged in the buffer the last slice leaves.
+namespace b3 {
+constexpr int BM = 128, BN = 256, BK = 64, NS = 3, WM = 2, WN = 4, MF = 32;
+constexpr int NW = WM * WN, kThreads = NW * kWave;
+constexpr int TM = BM / WM, TN = BN / WN, FM = TM / MF, FN = TN / MF;
+constexpr int ROWB = BK * 2, CPR = ROWB / 16;
+constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB, STAGE = A_BYTES + B_BYTES;
+constexpr int QA = A_BYTES / 1024 / NW, QB = B_BYTES / 1024 / NW, Q = QA + QB;
+constexpr int HSTR = BN + 16;                       // staged row: BN/2 bf16 + 16 bytes
+constexpr int ROWTAB = NS * STAGE;                  // output row of each tile row (GEMM 2)
+constexpr int kLdsBytes = ROWTAB + BM * 4;
+static_assert(BM * HSTR <= STAGE, "the epilogue is staged in one stage buffer");
+static_assert(kLdsBytes <= 160 * 1024, "LDS per CU");
+static_assert(QA * NW * 1024 == A_BYTES && QB * NW * 1024 == B_BYTES, "loads split over the waves");
+static_assert(FM * MF == TM && FN * MF == TN && FM == 2 && FN == 2, "wave tile");
+static_assert(kThreads >= BM, "one tile row per thread in the row table");
+static_assert(Q < 16, "vmcnt immediates");
+constexpr int kWavesPerSimd = NW / 4;
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+struct Tile {
+    int m0, n0, rows, fa, obase, orow;
+    const uint8_t* bbase;
+    uint32_t ao[QA];
+};
+
+__device__ __forceinline__ Tile make_tile(const GemmArgs& a, int lid, int n_tiles) {
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int wm = wave / WN;
+    Tile t;
+    const int slot = lid / n_tiles;
+    int nt = lid % n_tiles;
+    const int tinfo = a.tiles[1 + slot];
+    const int ei = tinfo >> 16;
+    int mt = tinfo & 0xFFFF;
+    const int entry = a.list.ent[ei];
+    const int e = entry & 1023;
+    const bool shared = e == kSharedTag;
+    const uint8_t* blob = shared ? a.shared_blob : a.slot_base + int64_t(entry >> 10) * a.blob_bytes;
+    const int base = shared ? 0 : a.offsets[e];
+    t.rows = shared ? a.T : a.offsets[e + 1] - base;
+    if (t.rows <= a.N) {                        // rows in fewer bytes than the weights: m-tiles fastest
+        const int mte = (t.rows + BM - 1) / BM;
+        const int off = lid - n_tiles * (slot - mt);
+        nt = off / mte;
+        mt = off % mte;
+    }
+    t.m0 = mt * BM;
+    t.n0 = nt * BN;
+    const int fa = (t.rows - t.m0 - wm * TM + 31) / 32;
+    t.fa = __builtin_amdgcn_readfirstlane(fa < 0 ? 0 : fa > FM ? FM : fa);
+    const uint32_t arow_bytes = uint32_t(a.K) * 2;
+    const uint32_t c16 = uint32_t(swz((wave * 64 + lane) / CPR, lane % CPR)) * 16;
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+        const int r = ((wave + NW * q) * 64 + lane) / CPR;
+        const int rr = t.m0 + r < t.rows ? t.m0 + r : 0;
+        uint32_t srow;
+        if (a.mode == 0)
+            srow = shared ? rr : a.perm[base + rr] / a.k;
+        else
+            srow = shared ? a.T * a.k + rr : base + rr;
+        t.ao[q] = srow * arow_bytes + c16;
+    }
+    t.bbase = blob + a.off_w + int64_t(t.n0) * a.K * 2;
+    t.obase = (shared ? a.T * a.k : base) + t.m0;
+    const int r = tid;
+    t.orow = r >= BM || t.m0 + r >= t.rows ? -1 : a.mode == 0 || shared ? t.obase + r : a.perm[base + t.m0 + r];
+    return t;
+}
+
+// Loads of K slice ks of tile t into stage buffer buf (Q instructions a wave).
+__device__ __forceinline__ void issue(uint8_t* lds8, const GemmArgs& a, const Tile& t, int ks, int buf) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    uint8_t* st = lds8 + buf * STAGE;
+    const uint32_t koff = uint32_t(ks) * ROWB;
+    const uint32_t brow = uint32_t((wave * 64 + lane) / CPR);             // weight row of load QA
+    const uint32_t boff = brow * uint32_t(a.K) * 2 + uint32_t(swz(int(brow), lane % CPR)) * 16;
+    const uint32_t bstride = uint32_t(a.K) * 2 * (NW * 64 / CPR);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const uint8_t* src = q < QA ? a.a_src + (t.ao[q] + koff) : t.bbase + (boff + (q - QA) * bstride + koff);
+        __builtin_amdgcn_global_load_lds(src, st + (wave + NW * q) * 1024, 16, 0, 0);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+}  // namespace b3
+
+// One tile for a wave that computes FA fragment rows (0..2); slice ks is in buffer (g0 + ks) % 3.
+// On entry slices 0, 1 and 2 have been issued (in that order; the loads still outstanding are
+// at most those three).  On exit every load and store has completed; the caller issues the next
+// tile's slice 2 into buffer (g0 + nk - 1) % 3 (its slices 0 and 1 were issued here).
+template <int MODE, int FA>
+__device__ __forceinline__ void b3_tile(const GemmArgs& a, uint8_t* lds8, const b3::Tile& t, const b3::Tile& nx,
+                                        bool has_next, int g0) {
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int wm = wave / b3::WN, wn = wave % b3::WN;
+    const int nk = a.K / b3::BK;
+    constexpr int NA = FA > 0 ? FA : 1;
+    f32x16 acc[NA][b3::FN];
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+        for (int j = 0; j < b3::FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    auto buf_of = [&](int ks) { int b = g0 + ks; b -= 3 * (b / 3); return b; };
+    auto frag = [&](const uint8_t* as_, int kk, bf16x8 (&fa)[NA], bf16x8 (&fb)[b3::FN]) {
+        const uint8_t* bs_ = as_ + b3::A_BYTES;
+        const int c = kk * 2 + lane / 32;
+#pragma unroll
+        for (int i = 0; i < FA; ++i) {
+            const int R = wm * b3::TM + i * 32 + lane % 32;
+            fa[i] = *reinterpret_cast<const bf16x8*>(as_ + R * b3::ROWB + (b3::swz(R, c) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < b3::FN; ++j) {
+            const int R = wn * b3::TN + j * 32 + lane % 32;
+            fb[j] = *reinterpret_cast<const bf16x8*>(bs_ + R * b3::ROWB + (b3::swz(R, c) << 4));
+        }
+    };
+    auto mma = [&](const bf16x8 (&fa)[NA], const bf16x8 (&fb)[b3::FN]) {
+#pragma unroll
+        for (int i = 0; i < FA; ++i)
+#pragma unroll
+            for (int j = 0; j < b3::FN; ++j) acc[i][j] = mfma(fa[i], fb[j], acc[i][j]);
+    };
+    constexpr int NM = FA * b3::FN, NR = FA + b3::FN;
+    auto sched = [&]() {
+        if constexpr (NM >= NR && NR > 0) {
+#pragma unroll
+            for (int n = 0; n < NR; ++n) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if constexpr (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+        }
+    };
+    bf16x8 fa0[NA], fb0[b3::FN], fa1[NA], fb1[b3::FN];
+    b3::wait_vm<2 * b3::Q>();           // slice 0 landed (slices 1 and 2 may still be in flight)
+    b3::bare_barrier();
+    if (MODE == 1 && tid < b3::BM) reinterpret_cast<int32_t*>(lds8 + b3::ROWTAB)[tid] = t.orow;   // read after later barriers
+    if constexpr (FA > 0) frag(lds8 + buf_of(0) * b3::STAGE, 0, fa0, fb0);
+    for (int ks = 0; ks + 1 < nk; ++ks) {
+        const uint8_t* as_ = lds8 + buf_of(ks) * b3::STAGE;
+        if constexpr (FA > 0) {
+            frag(as_, 1, fa1, fb1);
+            mma(fa0, fb0);
+            frag(as_, 2, fa0, fb0);
+            mma(fa1, fb1);
+            frag(as_, 3, fa1, fb1);
+            mma(fa0, fb0);
+            sched();
+            sched();
+            sched();
+        }
+        // every wave has read slice ks (its buffer can take slice ks + 3) and slice ks + 1 has
+        // landed (slice ks + 2, issued one slice later, may still be in flight)
+        b3::wait_vm<b3::Q>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): the fragment reads of this wave done
+        b3::bare_barrier();
+        {
+            // slice ks + 3 into the buffer slice ks leaves: this tile's, else the next tile's slice
+            // 0 or 1 (or, after the last tile, slice ks again: the same bytes, never read)
+            const int kn = ks + 3;
+            if (kn < nk) b3::issue(lds8, a, t, kn, buf_of(ks));
+            else if (has_next) b3::issue(lds8, a, nx, kn - nk, buf_of(ks));
+            else b3::issue(lds8, a, t, ks, buf_of(ks));
+        }
+        if constexpr (FA > 0) {
+            frag(lds8 + buf_of(ks + 1) * b3::STAGE, 0, fa0, fb0);
+            mma(fa1, fb1);
+            sched();
+        }
+    }
+    if constexpr (FA > 0) {
+        const uint8_t* as_ = lds8 + buf_of(nk - 1) * b3::STAGE;
+        frag(as_, 1, fa1, fb1);
+        mma(fa0, fb0);
+        frag(as_, 2, fa0, fb0);
+        mma(fa1, fb1);
+        frag(as_, 3, fa1, fb1);
+        mma(fa0, fb0);
+        mma(fa1, fb1);
+    }
+    // Epilogue staged in the buffer of the last slice (the next tile's slices 0 and 1 are
+    // loading into the other two); afterwards the next tile's slice 2 goes there.
+    uint8_t* stg = lds8 + buf_of(nk - 1) * b3::STAGE;
+    __syncthreads();            // every wave is done with slice nk - 1
+    if (MODE == 0) {
+#pragma unroll
+        for (int i = 0; i < FA; ++i)
+#pragma unroll
+            for (int j = 0; j < b3::FN; ++j) {
+                const int col = (wn * b3::TN + j * 32) / 2 + lane % 16;
+                float hv[8];
+#pragma unroll
+                for (int qq = 0; qq < 8; ++qq) {
+                    const int q1 = (qq / 4) * 8 + qq % 4;
+                    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[i][j][q1]),
+                                                                     __float_as_uint(acc[i][j][q1 + 4]), false, false);
+                    hv[qq] = ffn::silu_fast(__uint_as_float(sw[0])) * __uint_as_float(sw[1]);
+                }
+#pragma unroll
+                for (int qq = 0; qq < 8; ++qq) {
+                    const int q1 = (qq / 4) * 8 + qq % 4;
+                    const int q = (lane % 32) < 16 ? q1 : q1 + 4;
+                    const int r = wm * b3::TM + i * 32 + 8 * (q / 4) + (lane / 32) * 4 + (q % 4);
+                    *reinterpret_cast<uint16_t*>(stg + r * b3::HSTR + col * 2) = bf16_bits(hv[qq]);
+                }
+            }
+        __syncthreads();
+        constexpr int CH = b3::BN / 16;
+        uint16_t* h = static_cast<uint16_t*>(a.out);
+#pragma unroll 4
+        for (int idx = tid; idx < b3::BM * CH; idx += b3::kThreads) {
+            const int r = idx / CH, c = idx % CH;
+            if (t.m0 + r < t.rows)
+                *reinterpret_cast<dev::u32x4*>(h + int64_t(t.obase + r) * a.I + t.n0 / 2 + c * 8) =
+                    *reinterpret_cast<const dev::u32x4*>(stg + r * b3::HSTR + c * 16);
+        }
+    } else {
+        uint16_t* o = static_cast<uint16_t*>(a.out);
+        const int32_t* orow = reinterpret_cast<const int32_t*>(lds8 + b3::ROWTAB);
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+            for (int i = 0; i < FA; ++i)
+#pragma unroll
+                for (int jj = 0; jj < b3::FN / 2; ++jj) {
+                    const int col = wn * (b3::TN / 2) + jj * 32 + lane % 32;
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const int r = wm * b3::TM + i * 32 + 8 * (q / 4) + (lane / 32) * 4 + (q % 4);
+                        *reinterpret_cast<uint16_t*>(stg + r * b3::HSTR + col * 2) =
+                            bf16_bits(acc[i][b3::FN / 2 * pass + jj][q]);
+                    }
+                }
+            __syncthreads();
+            constexpr int CW = b3::TN / 16;
+#pragma unroll 4
+            for (int idx = tid; idx < b3::BM * 16; idx += b3::kThreads) {
+                const int r = idx / 16, c = idx % 16;
+                const int d = orow[r];
+                if (d >= 0)
+                    *reinterpret_cast<dev::u32x4*>(o + int64_t(d) * a.H + t.n0 + (c / CW) * b3::TN + pass * (b3::TN / 2) +
+                                                   (c % CW) * 8) = *reinterpret_cast<const dev::u32x4*>(stg + r * b3::HSTR + c * 16);
+            }
+            if (pass == 0) __syncthreads();
+        }
+    }
+    __syncthreads();            // the staging is read
+    __builtin_amdgcn_s_waitcnt(0);   // the stores and every load issued so far have completed
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(b3::kThreads) __attribute__((amdgpu_waves_per_eu(b3::kWavesPerSimd, b3::kWavesPerSimd)))
+k_gemm_b3(const GemmArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
+    const int n_tiles = a.N / b3::BN;
+    const int total = a.tiles[0] * n_tiles;
+    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const int x = blockIdx.x % kXcds, stride = gridDim.x / kXcds;
+    int i = blockIdx.x / kXcds;
+    if (i >= per_xcd || x * per_xcd + i >= total) return;
+    const int nk = a.K / b3::BK;
+    // the tile descriptors are read while no slice is in flight (their loads would otherwise
+    // wait for the slices ahead of them)
+    b3::Tile cur = b3::make_tile(a, x * per_xcd + i, n_tiles);
+    int in = i + stride;
+    bool has_next = in < per_xcd && x * per_xcd + in < total;
+    b3::Tile nx = has_next ? b3::make_tile(a, x * per_xcd + in, n_tiles) : cur;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) b3::issue(lds8, a, cur, s, s);
+    int g0 = 0;
+    while (true) {
+        switch (cur.fa) {
+            case 2: b3_tile<MODE, 2>(a, lds8, cur, nx, has_next, g0); break;
+            case 1: b3_tile<MODE, 1>(a, lds8, cur, nx, has_next, g0); break;
+            default: b3_tile<MODE, 0>(a, lds8, cur, nx, has_next, g0); break;
+        }
+        if (!has_next) break;
+        g0 = (g0 + nk) % 3;
+        i = in;
+        in = i + stride;
+        const bool has_next2 = in < per_xcd && x * per_xcd + in < total;
+        const b3::Tile nn = has_next2 ? b3::make_tile(a, x * per_xcd + in, n_tiles) : nx;
+        b3::issue(lds8, a, nx, 2, (g0 + 2) % 3);       // the new tile's slices 0 and 1 are loaded
+        cur = nx;
+        nx = nn;
+        has_next = has_next2;
+    }
+}
+
 // The GEMM stages use more than the default 64 KiB of LDS per workgroup.
 hipError_t allow_lds() {
     static hipError_t once = [] {
@@ -1116,6 +1428,11 @@ hipError_t allow_lds() {
                              reinterpret_cast<const void*>(&k_gemm_big<1, false>)};
         for (const void* k : kb) {
             hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, big::Lay<false>::kLdsBytes);
+            if (e != hipSuccess) return e;
+        }
+        const void* k3[2] = {reinterpret_cast<const void*>(&k_gemm_b3<0>), reinterpret_cast<const void*>(&k_gemm_b3<1>)};
+        for (const void* k : k3) {
+            hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, b3::kLdsBytes);
             if (e != hipSuccess) return e;
         }
         const void* kf[2] = {reinterpret_cast<const void*>(&k_gemm_big<0, true>),
@@ -1152,11 +1469,13 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     const WsLayout W = ws_layout(c, T);
     int32_t* tiles = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + W.tiles);
     const bool fp4 = c.w_dtype == MOE_W_MXFP4;
-    // kernel per GEMM: 2 large-tile, 1 pipelined 128 x 256, 0 register-staged (MXFP4 shapes the
-    // large tile does not take; every bf16 shape gemm_shape_supported accepts fits the pipelined kernel).
-    // The large tile needs long K loops to pay for its per-tile start and epilogue at one
-    // workgroup per CU (measured on the 8K-token chunk of the 2048 x 768 layer: 547 us against
-    // 643 us for GEMM 1 with K = 2048, about even for GEMM 2 with K = 768).
+    // kernel per GEMM: 2 large-tile, 3 three-stage 128 x 256, 1 pipelined 128 x 256 (bf16 with
+    // fewer than three K slices of 64), 0 register-staged (MXFP4 shapes the large tile does not
+    // take; every bf16 shape gemm_shape_supported accepts fits 3 or 1).  The large tile needs
+    // long K loops to pay for its per-tile start and epilogue (measured on the 8K-token chunk of
+    // the 2048 x 768 layer: 547 us against 643 us for the pipelined kernel on GEMM 1 with
+    // K = 2048, about even on GEMM 2 with K = 768); on GEMM 1 the three-stage kernel ran 48 us
+    // slower than the large tile, on GEMM 2 (K = 768) 28 us faster than the pipelined kernel.
     auto kind = [&](int N, int K) {
         // large tile: an even slice count, A row offsets (rows of x or h times the row bytes)
         // in 32 bits and, for MXFP4, the tile's scales within their LDS region
@@ -1164,10 +1483,11 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
         const bool big_ok = N % big::BN == 0 && K % (2 * big::BK) == 0 &&
                             a_rows * K * 2 < (int64_t(1) << 32) && (!fp4 || K <= big::kMaxKFp4);
         if (fp4) return big_ok ? 2 : 0;
+        const bool b3_ok = N % b3::BN == 0 && K % b3::BK == 0 && K / b3::BK >= 3 && a_rows * K * 2 < (int64_t(1) << 32);
         if (K >= 2048 && big_ok) return 2;
-        return 1;
+        return b3_ok ? 3 : 1;
     };
-    auto bm_of = [](int kd) { return kd == 2 ? big::BM : kd == 1 ? dma::BM : BM; };
+    auto bm_of = [](int kd) { return kd == 3 ? b3::BM : kd == 2 ? big::BM : kd == 1 ? dma::BM : BM; };
     const int kind1 = kind(2 * c.inter, c.hidden), kind2 = kind(c.hidden, c.inter);
     TileMapArgs tm;
     tm.offsets = offsets;
@@ -1192,10 +1512,10 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     a.list = list;
     if ((e = allow_lds()) != hipSuccess) return e;
     auto launch = [&](int kd, int mode, int bm) {
-        const int bn = kd == 2 ? big::BN : kd == 1 ? dma::BN : BN;
+        const int bn = kd == 3 ? b3::BN : kd == 2 ? big::BN : kd == 1 ? dma::BN : BN;
         a.grid = (max_tiles(c, T, bm) * (a.N / bn) + kXcds - 1) / kXcds * kXcds;
         a.mode = mode;
-        if (kd == 2) {
+        if (kd == 2 || kd == 3) {
             // persistent: at most one workgroup per CU (a multiple of the XCD count)
             static const int n_cu = [] {
                 int dev = 0, n = 0;
@@ -1207,7 +1527,10 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
             const int cap = n_cu >= kXcds ? n_cu / kXcds * kXcds : kXcds;
             a.grid = a.grid < cap ? a.grid : cap;
             const dim3 g(a.grid), b(big::kThreads);
-            if (fp4) {
+            if (kd == 3) {
+                if (mode == 0) hipLaunchKernelGGL((k_gemm_b3<0>), g, dim3(b3::kThreads), b3::kLdsBytes, s, a);
+                else hipLaunchKernelGGL((k_gemm_b3<1>), g, dim3(b3::kThreads), b3::kLdsBytes, s, a);
+            } else if (fp4) {
                 if (mode == 0) hipLaunchKernelGGL((k_gemm_big<0, true>), g, b, big::Lay<true>::kLdsBytes, s, a);
                 else hipLaunchKernelGGL((k_gemm_big<1, true>), g, b, big::Lay<true>::kLdsBytes, s, a);
             } else {
