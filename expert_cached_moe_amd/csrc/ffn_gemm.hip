@@ -713,6 +713,7 @@ struct Tile {
     const uint8_t* bbase;       // weight row n0 at K offset 0 (wave-uniform)
     const uint8_t* sbase;       // MXFP4: the e8m0 scales of weight row n0 (wave-uniform)
     uint32_t ao[QA];            // byte offsets (from a_src) of the A rows of this lane's QA load chunks
+    uint32_t alive;             // bit q: A load q of this wave covers a row of the tile (wave-uniform)
 };
 
 // Byte offset of this lane's chunk within a weight-row block: load QA + q reads weight row
@@ -757,9 +758,13 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& a, int lid, int n_tile
     t.fa = __builtin_amdgcn_readfirstlane(fa < 0 ? 0 : fa > FM ? FM : fa);
     const uint32_t arow_bytes = uint32_t(a.K) * 2;
     const uint32_t c16 = uint32_t(lane_chunk()) * 16;
+    t.alive = 0;
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
         const int r = ((wave + NW * q) * 64 + lane) / CPR;
+        // A load q of the wave fills tile rows 8 (wave + NW q) .. + 7; one wholly past the
+        // expert's rows is skipped (its LDS rows feed only output rows that are dropped)
+        if (t.m0 + (wave + NW * q) * (64 / CPR) < t.rows) t.alive |= 1u << q;
         const int rr = t.m0 + r < t.rows ? t.m0 + r : 0;        // rows past the end load row 0 (dropped)
         uint32_t srow;
         if (a.mode == 0)
@@ -768,6 +773,7 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& a, int lid, int n_tile
             srow = shared ? a.T * a.k + rr : base + rr;
         t.ao[q] = srow * arow_bytes + c16;
     }
+    t.alive = __builtin_amdgcn_readfirstlane(t.alive);
     t.bbase = blob + a.off_w + int64_t(t.n0) * (FP4 ? a.K / 2 : a.K * 2);
     t.sbase = blob + a.off_s + int64_t(t.n0) * (a.K / 32);
     t.obase = (shared ? a.T * a.k : base) + t.m0;
@@ -794,16 +800,20 @@ __device__ __forceinline__ uint32_t b_stride(int K) {
     return FP4 ? 0u : uint32_t(K) * 2 * (NW * 64 / CPR);
 }
 
-// Loads of one K slice into stage buffer buf: A rows at a_src + ao[q] + koa, weight rows at
-// bbase + boff + kob.
-template <bool FP4>
-__device__ __forceinline__ void issue(uint8_t* lds8, const uint8_t* a_src, const uint32_t (&ao)[QA],
+// Loads of one K slice into stage buffer buf: A rows at a_src + ao[q] + koa (with SKIP, the
+// loads in alive only), weight rows at bbase + boff + kob.  The slice is handed over by a
+// barrier that waits for every load, so the number issued may vary.  Skipping is used by the
+// down GEMM (MXFP4 8K chunk: 843-850 us against 895-899 us); on the gate/up GEMMs it measured
+// no faster (bf16: 458 against 445 us), so they load every row group.
+template <bool FP4, bool SKIP>
+__device__ __forceinline__ void issue(uint8_t* lds8, const uint8_t* a_src, const uint32_t (&ao)[QA], uint32_t alive,
                                       const uint8_t* bbase, uint32_t boff, uint32_t bstride, uint32_t koa, uint32_t kob,
                                       int buf) {
     const int wave = threadIdx.x / kWave;
     uint8_t* st = lds8 + buf * Lay<FP4>::STAGE;
 #pragma unroll
     for (int q = 0; q < Lay<FP4>::Q; ++q) {
+        if (SKIP && q < QA && !((alive >> q) & 1u)) continue;
         const uint8_t* src = q < QA ? a_src + (ao[q] + koa) : bbase + (boff + (q - QA) * bstride + kob);
         __builtin_amdgcn_global_load_lds(src, st + (wave + NW * q) * 1024, 16, 0, 0);
     }
@@ -942,7 +952,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
     // the accumulators in place across iterations.
     bf16x8 fa0[NA], fb0[big::FN], fa1[NA], fb1[big::FN];
     barrier_loads();            // slice 0 (and the scales) landed; the previous tile is done with the LDS
-    big::issue<FP4>(lds8, a.a_src, t.ao, t.bbase, boff, bstride, big::ROWB, L::BROWB, 1);
+    big::issue<FP4, MODE == 1>(lds8, a.a_src, t.ao, t.alive, t.bbase, boff, bstride, big::ROWB, L::BROWB, 1);
     if (MODE == 1 && tid < big::BM) reinterpret_cast<int32_t*>(lds8 + L::ROWTAB)[tid] = t.orow;   // read after later barriers
     if constexpr (FA > 0) frag(lds8, 0, 0, fa0, fb0);
     for (int ks = 0; ks + 1 < nk; ++ks) {
@@ -972,7 +982,8 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
             uint32_t ao[big::QA];
 #pragma unroll
             for (int q = 0; q < big::QA; ++q) ao[q] = other ? nx.ao[q] : t.ao[q];
-            big::issue<FP4>(lds8, a.a_src, ao, other ? nx.bbase : t.bbase, boff, bstride, kn * big::ROWB, kn * L::BROWB,
+            big::issue<FP4, MODE == 1>(lds8, a.a_src, ao, other ? nx.alive : t.alive, other ? nx.bbase : t.bbase, boff, bstride,
+                            kn * big::ROWB, kn * L::BROWB,
                             ks & 1);
         }
         if constexpr (FA > 0) {
@@ -1082,7 +1093,7 @@ k_gemm_big(const GemmArgs a) {
     int i = blockIdx.x / kXcds;
     if (i >= per_xcd || x * per_xcd + i >= total) return;
     big::Tile cur = big::make_tile<FP4>(a, x * per_xcd + i, n_tiles);
-    big::issue<FP4>(lds8, a.a_src, cur.ao, cur.bbase, big::b_lane_off<FP4>(a.K), big::b_stride<FP4>(a.K), 0, 0, 0);
+    big::issue<FP4, MODE == 1>(lds8, a.a_src, cur.ao, cur.alive, cur.bbase, big::b_lane_off<FP4>(a.K), big::b_stride<FP4>(a.K), 0, 0, 0);
     if (FP4) big::issue_scales(lds8, cur.sbase, a.K);
     while (true) {
         const int in = i + stride;
