@@ -1044,36 +1044,36 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
                     *reinterpret_cast<const dev::u32x4*>(stg + r * big::HSTR + c * 16);
         }
     } else {
-        // pair outputs, bf16, staged in two passes of half the tile's columns (fragments
-        // j = FN/2 pass .. FN/2 pass + FN/2 - 1 of every wave: BN/2 columns, a run of TN bytes
-        // per row for each wave column), then written as whole lines to the rows from the
-        // tile's row table
+        // pair outputs, bf16, staged in two passes of half the tile's columns (pass p: columns
+        // BN/2 p .. BN/2 p + BN/2 - 1, those of wave columns WN/2 p .. WN/2 p + WN/2 - 1), then
+        // each row's BN/2 contiguous columns written as whole lines to the row from the tile's
+        // row table
         uint16_t* o = static_cast<uint16_t*>(a.out);
         const int32_t* orow = reinterpret_cast<const int32_t*>(lds8 + L::ROWTAB);
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
+            if (wn / (big::WN / 2) == pass) {
 #pragma unroll
-            for (int i = 0; i < FA; ++i)
+                for (int i = 0; i < FA; ++i)
 #pragma unroll
-                for (int jj = 0; jj < big::FN / 2; ++jj) {
-                    const int col = wn * (big::TN / 2) + jj * 32 + lane % 32;     // staged column
+                    for (int j = 0; j < big::FN; ++j) {
+                        const int col = (wn % (big::WN / 2)) * big::TN + j * 32 + lane % 32;     // staged column
 #pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        const int r = wm * big::TM + i * 32 + 8 * (q / 4) + (lane / 32) * 4 + (q % 4);
-                        *reinterpret_cast<uint16_t*>(stg + r * big::HSTR + col * 2) =
-                            bf16_bits(acc[i][big::FN / 2 * pass + jj][q]);
+                        for (int q = 0; q < 16; ++q) {
+                            const int r = wm * big::TM + i * 32 + 8 * (q / 4) + (lane / 32) * 4 + (q % 4);
+                            *reinterpret_cast<uint16_t*>(stg + r * big::HSTR + col * 2) = bf16_bits(acc[i][j][q]);
+                        }
                     }
-                }
+            }
             __syncthreads();
-            // 16 chunks of 16 bytes per staged row; wave column w's run is chunks CW w .. CW w + CW - 1
-            constexpr int CW = big::TN / 16;
+            // 16 chunks of 16 bytes per staged row: 256 contiguous bytes of the output row
 #pragma unroll 4
             for (int idx = tid; idx < big::BM * 16; idx += big::kThreads) {
                 const int r = idx / 16, c = idx % 16;
                 const int d = orow[r];
                 if (d >= 0)
-                    *reinterpret_cast<dev::u32x4*>(o + int64_t(d) * a.H + t.n0 + (c / CW) * big::TN + pass * (big::TN / 2) +
-                                                   (c % CW) * 8) = *reinterpret_cast<const dev::u32x4*>(stg + r * big::HSTR + c * 16);
+                    *reinterpret_cast<dev::u32x4*>(o + int64_t(d) * a.H + t.n0 + pass * (big::BN / 2) + c * 8) =
+                        *reinterpret_cast<const dev::u32x4*>(stg + r * big::HSTR + c * 16);
             }
             if (pass == 0) __syncthreads();
         }
@@ -1354,27 +1354,27 @@ __device__ __forceinline__ void b3_tile(const GemmArgs& a, uint8_t* lds8, const 
         const int32_t* orow = reinterpret_cast<const int32_t*>(lds8 + b3::ROWTAB);
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
+            if (wn / (b3::WN / 2) == pass) {
 #pragma unroll
-            for (int i = 0; i < FA; ++i)
+                for (int i = 0; i < FA; ++i)
 #pragma unroll
-                for (int jj = 0; jj < b3::FN / 2; ++jj) {
-                    const int col = wn * (b3::TN / 2) + jj * 32 + lane % 32;
+                    for (int j = 0; j < b3::FN; ++j) {
+                        const int col = (wn % (b3::WN / 2)) * b3::TN + j * 32 + lane % 32;     // staged column
 #pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        const int r = wm * b3::TM + i * 32 + 8 * (q / 4) + (lane / 32) * 4 + (q % 4);
-                        *reinterpret_cast<uint16_t*>(stg + r * b3::HSTR + col * 2) =
-                            bf16_bits(acc[i][b3::FN / 2 * pass + jj][q]);
+                        for (int q = 0; q < 16; ++q) {
+                            const int r = wm * b3::TM + i * 32 + 8 * (q / 4) + (lane / 32) * 4 + (q % 4);
+                            *reinterpret_cast<uint16_t*>(stg + r * b3::HSTR + col * 2) = bf16_bits(acc[i][j][q]);
+                        }
                     }
-                }
+            }
             __syncthreads();
-            constexpr int CW = b3::TN / 16;
 #pragma unroll 4
             for (int idx = tid; idx < b3::BM * 16; idx += b3::kThreads) {
                 const int r = idx / 16, c = idx % 16;
                 const int d = orow[r];
                 if (d >= 0)
-                    *reinterpret_cast<dev::u32x4*>(o + int64_t(d) * a.H + t.n0 + (c / CW) * b3::TN + pass * (b3::TN / 2) +
-                                                   (c % CW) * 8) = *reinterpret_cast<const dev::u32x4*>(stg + r * b3::HSTR + c * 16);
+                    *reinterpret_cast<dev::u32x4*>(o + int64_t(d) * a.H + t.n0 + pass * (b3::BN / 2) + c * 8) =
+                        *reinterpret_cast<const dev::u32x4*>(stg + r * b3::HSTR + c * 16);
             }
             if (pass == 0) __syncthreads();
         }
