@@ -86,6 +86,7 @@ struct TileMapArgs {
     const int32_t* offsets;
     int32_t T, bm;            // bm: row-tile height of the GEMM kernel that reads the list
     int32_t* tiles;   // [0]: count, then (entry << 16) | m_tile
+    int4* rec;        // per row tile: list entry, first row (in perm order), rows, m_tile
     ExpertList list;
 };
 
@@ -129,8 +130,15 @@ __global__ void __launch_bounds__(1024) k_tile_map(const TileMapArgs a) {
         }
     }
     __syncthreads();
-    for (int i = tid; i < n; i += blockDim.x)
-        for (int m = 0; m < s_cnt[i]; ++m) a.tiles[1 + s_base[i] + m] = (i << 16) | m;
+    for (int i = tid; i < n; i += blockDim.x) {
+        const int ent = a.list.ent[i], e = ent & 1023;
+        const int base = e == kSharedTag ? 0 : a.offsets[e];
+        const int rows = e == kSharedTag ? a.T : a.offsets[e + 1] - base;
+        for (int m = 0; m < s_cnt[i]; ++m) {
+            a.tiles[1 + s_base[i] + m] = (i << 16) | m;
+            a.rec[s_base[i] + m] = make_int4(ent, base, rows, m);
+        }
+    }
 }
 
 struct GemmArgs {
@@ -143,6 +151,7 @@ struct GemmArgs {
     const int32_t* offsets;
     const int32_t* perm;
     const int32_t* tiles;
+    const int4* rec;           // per row tile: list entry, first row, rows, m_tile (one load)
     int32_t T, k, K, N;        // K: reduction length, N: output columns of the matrix
     int32_t I, H;
     int32_t grid;              // launched workgroups (a multiple of the XCD count)
@@ -724,22 +733,21 @@ __device__ __forceinline__ int lane_chunk() {
     return swz((wave * 64 + lane) / CPR, lane % CPR);
 }
 
-template <bool FP4>
+template <int MODE, bool FP4>
 __device__ __forceinline__ Tile make_tile(const GemmArgs& a, int lid, int n_tiles) {
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave / WN;
     Tile t;
     const int slot = lid / n_tiles;
     int nt = lid % n_tiles;
-    const int tinfo = a.tiles[1 + slot];
-    const int ei = tinfo >> 16;
-    int mt = tinfo & 0xFFFF;
-    const int entry = a.list.ent[ei];
+    const int4 rec = a.rec[slot];                   // one load instead of a chain of four
+    const int entry = rec.x;
+    int mt = rec.w;
     const int e = entry & 1023;
     const bool shared = e == kSharedTag;
     const uint8_t* blob = shared ? a.shared_blob : a.slot_base + int64_t(entry >> 10) * a.blob_bytes;
-    const int base = shared ? 0 : a.offsets[e];
-    t.rows = shared ? a.T : a.offsets[e + 1] - base;
+    const int base = rec.y;
+    t.rows = rec.z;
     if (int64_t(t.rows) * 64 <= int64_t(a.N) * (FP4 ? 17 : 64)) {
         // the expert's activation rows take fewer bytes than its weights (bf16: 2 bytes an
         // element; MXFP4: 17/32): its m-tiles run fastest, so the tiles that share a weight
@@ -758,6 +766,7 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& a, int lid, int n_tile
     t.fa = __builtin_amdgcn_readfirstlane(fa < 0 ? 0 : fa > FM ? FM : fa);
     const uint32_t arow_bytes = uint32_t(a.K) * 2;
     const uint32_t c16 = uint32_t(lane_chunk()) * 16;
+    int pv[QA], rrs[QA];
     t.alive = 0;
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
@@ -766,19 +775,31 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& a, int lid, int n_tile
         // expert's rows is skipped (its LDS rows feed only output rows that are dropped)
         if (t.m0 + (wave + NW * q) * (64 / CPR) < t.rows) t.alive |= 1u << q;
         const int rr = t.m0 + r < t.rows ? t.m0 + r : 0;        // rows past the end load row 0 (dropped)
-        uint32_t srow;
-        if (a.mode == 0)
-            srow = shared ? rr : a.perm[base + rr] / a.k;
-        else
-            srow = shared ? a.T * a.k + rr : base + rr;
-        t.ao[q] = srow * arow_bytes + c16;
+        if constexpr (MODE == 0) {
+            rrs[q] = rr;
+            pv[q] = a.perm[shared ? 0 : base + rr];     // a valid index either way
+        } else {
+            t.ao[q] = uint32_t(shared ? a.T * a.k + rr : base + rr) * arow_bytes + c16;
+        }
+    }
+    if constexpr (MODE == 0) {
+        // the QA perm loads are all issued before the first of them is waited for
+#pragma unroll
+        for (int q = 0; q < QA; ++q) asm volatile("" : "+v"(pv[q]));
+#pragma unroll
+        for (int q = 0; q < QA; ++q)
+            t.ao[q] = (shared ? uint32_t(rrs[q]) : uint32_t(pv[q]) / uint32_t(a.k)) * arow_bytes + c16;
     }
     t.alive = __builtin_amdgcn_readfirstlane(t.alive);
     t.bbase = blob + a.off_w + int64_t(t.n0) * (FP4 ? a.K / 2 : a.K * 2);
     t.sbase = blob + a.off_s + int64_t(t.n0) * (a.K / 32);
     t.obase = (shared ? a.T * a.k : base) + t.m0;
     const int r = tid;                                           // epilogue: tile row tid
-    t.orow = r >= BM || t.m0 + r >= t.rows ? -1 : a.mode == 0 || shared ? t.obase + r : a.perm[base + t.m0 + r];
+    const bool live = r < BM && t.m0 + r < t.rows;
+    if constexpr (MODE == 0)
+        t.orow = live ? t.obase + r : -1;
+    else
+        t.orow = !live ? -1 : shared ? t.obase + r : a.perm[live && !shared ? base + t.m0 + r : 0];
     return t;
 }
 
@@ -865,12 +886,25 @@ __device__ __forceinline__ void barrier_loads() {
     __syncthreads();
 }
 
+// Barrier over LDS only: this wave's LDS operations have completed, vector memory operations
+// (the epilogue's global stores) may still be in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // One tile for a wave that computes FA fragment rows (0..FM).  On entry the tile's slice 0
-// is in flight into buffer 0; before the last slice the next tile's slice 0 is issued into
-// buffer 0 (for the last tile of the workgroup, a harmless reload of this tile's last slice).
+// is in flight into buffer 0 (first tile of the workgroup) or has landed (later tiles: the
+// previous tile waited for it before its epilogue's stores, so the stores are left to drain
+// under this tile's first slice); before the last slice the next tile's slice 0 is issued
+// into buffer 0 (for the last tile of the workgroup, a harmless reload of this tile's last
+// slice).  The epilogue also builds nn, the descriptor of tile nn_lid (if >= 0), while no
+// store is in flight.
 template <int MODE, int FA, bool FP4>
 __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const big::Tile& t, const big::Tile& nx,
-                                         bool has_next) {
+                                         bool has_next, bool first, int nn_lid, big::Tile& nn) {
     using L = big::Lay<FP4>;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave / big::WN, wn = wave % big::WN;
@@ -951,7 +985,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
     // sub-step).  The loop body is straight-line and the last slice is peeled, which keeps
     // the accumulators in place across iterations.
     bf16x8 fa0[NA], fb0[big::FN], fa1[NA], fb1[big::FN];
-    barrier_loads();            // slice 0 (and the scales) landed; the previous tile is done with the LDS
+    if (first) barrier_loads();     // slice 0 (and the scales) landed
     big::issue<FP4, MODE == 1>(lds8, a.a_src, t.ao, t.alive, t.bbase, boff, bstride, big::ROWB, L::BROWB, 1);
     if (MODE == 1 && tid < big::BM) reinterpret_cast<int32_t*>(lds8 + L::ROWTAB)[tid] = t.orow;   // read after later barriers
     if constexpr (FA > 0) frag(lds8, 0, 0, fa0, fb0);
@@ -968,7 +1002,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
             sched(RdK{});
             sched(RdK{});
         }
-        barrier_loads();
+        barrier_loads();            // (in the first slice of a later tile, also the previous epilogue's stores)
         // MXFP4: the next slice's first reads go before the loads that refill this slice's
         // buffer (in program order, so the code reads are not taken to depend on those
         // loads); bf16 issues the loads first (measured faster)
@@ -1006,8 +1040,19 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
     // Epilogue through the LDS above buffer 0 (buffer 0 is taking the next tile's first
     // slice): the tile is staged there and written out as whole rows, 16 bytes a lane.
     uint8_t* stg = lds8 + L::EPI;
-    __syncthreads();            // every wave is done with slice nk - 1 (buffer 1) and the scales
+    // Every wave is done with slice nk - 1 (buffer 1) and the scales, and the next tile's slice
+    // 0 has landed: the only vector memory operations in flight are loads here, so this wait
+    // costs their tail.  Loads and stores share one completion counter, so the loads the next
+    // tile needs first are waited for before any store is issued; the stores then drain under
+    // the next tile's first slice.
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
     if (FP4 && has_next) big::issue_scales(lds8, nx.sbase, a.K);   // the next tile's, while this one finishes
+    // the descriptor of the tile after next, and the scales, complete before the first store
+    auto next_desc = [&]() {
+        if (nn_lid >= 0) nn = big::make_tile<MODE, FP4>(a, nn_lid, a.N / big::BN);
+        __builtin_amdgcn_s_waitcnt(0);
+    };
     if (MODE == 0) {
         // SwiGLU: in a 32-wide fragment lanes 0-15 hold gate and lanes 16-31 up for the
         // same 16 h columns; permlane16_swap of elements q1 and q1+4 hands every lane a
@@ -1033,15 +1078,22 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
                     *reinterpret_cast<uint16_t*>(stg + r * big::HSTR + col * 2) = bf16_bits(hv[qq]);
                 }
             }
-        __syncthreads();
+        next_desc();
+        lds_barrier();
         constexpr int CH = big::BN / 16;                     // 16-byte chunks per h row of the tile
+        constexpr int PER = big::BM * CH / big::kThreads;
         uint16_t* h = static_cast<uint16_t*>(a.out);
-#pragma unroll 4
-        for (int idx = tid; idx < big::BM * CH; idx += big::kThreads) {
-            const int r = idx / CH, c = idx % CH;
+        dev::u32x4 v[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int idx = tid + k * big::kThreads, r = idx / CH, c = idx % CH;
+            v[k] = *reinterpret_cast<const dev::u32x4*>(stg + r * big::HSTR + c * 16);
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int idx = tid + k * big::kThreads, r = idx / CH, c = idx % CH;
             if (t.m0 + r < t.rows)
-                *reinterpret_cast<dev::u32x4*>(h + int64_t(t.obase + r) * a.I + t.n0 / 2 + c * 8) =
-                    *reinterpret_cast<const dev::u32x4*>(stg + r * big::HSTR + c * 16);
+                *reinterpret_cast<dev::u32x4*>(h + int64_t(t.obase + r) * a.I + t.n0 / 2 + c * 8) = v[k];
         }
     } else {
         // pair outputs, bf16, staged in two passes of half the tile's columns (pass p: columns
@@ -1065,19 +1117,29 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
                         }
                     }
             }
-            __syncthreads();
-            // 16 chunks of 16 bytes per staged row: 256 contiguous bytes of the output row
-#pragma unroll 4
-            for (int idx = tid; idx < big::BM * 16; idx += big::kThreads) {
-                const int r = idx / 16, c = idx % 16;
-                const int d = orow[r];
-                if (d >= 0)
-                    *reinterpret_cast<dev::u32x4*>(o + int64_t(d) * a.H + t.n0 + pass * (big::BN / 2) + c * 8) =
-                        *reinterpret_cast<const dev::u32x4*>(stg + r * big::HSTR + c * 16);
+            if (pass == 0) next_desc();
+            lds_barrier();
+            // 16 chunks of 16 bytes per staged row: 256 contiguous bytes of the output row; the
+            // LDS reads first, then the stores
+            constexpr int PER = big::BM * 16 / big::kThreads;
+            int32_t d[PER];
+            dev::u32x4 v[PER];
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int idx = tid + k * big::kThreads, r = idx / 16, c = idx % 16;
+                d[k] = orow[r];
+                v[k] = *reinterpret_cast<const dev::u32x4*>(stg + r * big::HSTR + c * 16);
             }
-            if (pass == 0) __syncthreads();
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int c = (tid + k * big::kThreads) % 16;
+                if (d[k] >= 0)
+                    *reinterpret_cast<dev::u32x4*>(o + int64_t(d[k]) * a.H + t.n0 + pass * (big::BN / 2) + c * 8) = v[k];
+            }
+            if (pass == 0) lds_barrier();
         }
     }
+    lds_barrier();              // the staging is read: the next tile's slice 1 goes into buffer 1
 }
 
 // Persistent: workgroup b serves XCD b % 8 and walks tiles b / 8, b / 8 + G / 8, ... of that
@@ -1092,23 +1154,33 @@ k_gemm_big(const GemmArgs a) {
     const int x = blockIdx.x % kXcds, stride = gridDim.x / kXcds;
     int i = blockIdx.x / kXcds;
     if (i >= per_xcd || x * per_xcd + i >= total) return;
-    big::Tile cur = big::make_tile<FP4>(a, x * per_xcd + i, n_tiles);
+    // the descriptors of the first two tiles are read before any load is issued; later ones
+    // in the epilogue two tiles ahead
+    big::Tile cur = big::make_tile<MODE, FP4>(a, x * per_xcd + i, n_tiles);
+    int in = i + stride;
+    bool has_next = in < per_xcd && x * per_xcd + in < total;
+    big::Tile nx = has_next ? big::make_tile<MODE, FP4>(a, x * per_xcd + in, n_tiles) : cur;
     big::issue<FP4, MODE == 1>(lds8, a.a_src, cur.ao, cur.alive, cur.bbase, big::b_lane_off<FP4>(a.K), big::b_stride<FP4>(a.K), 0, 0, 0);
     if (FP4) big::issue_scales(lds8, cur.sbase, a.K);
+    bool first = true;
     while (true) {
-        const int in = i + stride;
-        const bool has_next = in < per_xcd && x * per_xcd + in < total;
-        const big::Tile nx = has_next ? big::make_tile<FP4>(a, x * per_xcd + in, n_tiles) : cur;
+        const int in2 = in + stride;
+        const bool has_next2 = has_next && in2 < per_xcd && x * per_xcd + in2 < total;
+        const int nn_lid = has_next2 ? x * per_xcd + in2 : -1;
+        big::Tile nn = nx;
         switch (cur.fa) {
-            case 4: big_tile<MODE, 4, FP4>(a, lds8, cur, nx, has_next); break;
-            case 3: big_tile<MODE, 3, FP4>(a, lds8, cur, nx, has_next); break;
-            case 2: big_tile<MODE, 2, FP4>(a, lds8, cur, nx, has_next); break;
-            case 1: big_tile<MODE, 1, FP4>(a, lds8, cur, nx, has_next); break;
-            default: big_tile<MODE, 0, FP4>(a, lds8, cur, nx, has_next); break;
+            case 4: big_tile<MODE, 4, FP4>(a, lds8, cur, nx, has_next, first, nn_lid, nn); break;
+            case 3: big_tile<MODE, 3, FP4>(a, lds8, cur, nx, has_next, first, nn_lid, nn); break;
+            case 2: big_tile<MODE, 2, FP4>(a, lds8, cur, nx, has_next, first, nn_lid, nn); break;
+            case 1: big_tile<MODE, 1, FP4>(a, lds8, cur, nx, has_next, first, nn_lid, nn); break;
+            default: big_tile<MODE, 0, FP4>(a, lds8, cur, nx, has_next, first, nn_lid, nn); break;
         }
         if (!has_next) break;
         cur = nx;
-        i = in;
+        nx = nn;
+        has_next = has_next2;
+        in = in2;
+        first = false;
     }
 }
 
@@ -1145,21 +1217,21 @@ struct Tile {
     uint32_t ao[QA];
 };
 
+template <int MODE>
 __device__ __forceinline__ Tile make_tile(const GemmArgs& a, int lid, int n_tiles) {
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave / WN;
     Tile t;
     const int slot = lid / n_tiles;
     int nt = lid % n_tiles;
-    const int tinfo = a.tiles[1 + slot];
-    const int ei = tinfo >> 16;
-    int mt = tinfo & 0xFFFF;
-    const int entry = a.list.ent[ei];
+    const int4 rec = a.rec[slot];
+    const int entry = rec.x;
+    int mt = rec.w;
     const int e = entry & 1023;
     const bool shared = e == kSharedTag;
     const uint8_t* blob = shared ? a.shared_blob : a.slot_base + int64_t(entry >> 10) * a.blob_bytes;
-    const int base = shared ? 0 : a.offsets[e];
-    t.rows = shared ? a.T : a.offsets[e + 1] - base;
+    const int base = rec.y;
+    t.rows = rec.z;
     if (t.rows <= a.N) {                        // rows in fewer bytes than the weights: m-tiles fastest
         const int mte = (t.rows + BM - 1) / BM;
         const int off = lid - n_tiles * (slot - mt);
@@ -1172,21 +1244,34 @@ __device__ __forceinline__ Tile make_tile(const GemmArgs& a, int lid, int n_tile
     t.fa = __builtin_amdgcn_readfirstlane(fa < 0 ? 0 : fa > FM ? FM : fa);
     const uint32_t arow_bytes = uint32_t(a.K) * 2;
     const uint32_t c16 = uint32_t(swz((wave * 64 + lane) / CPR, lane % CPR)) * 16;
+    int pv[QA], rrs[QA];
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
         const int r = ((wave + NW * q) * 64 + lane) / CPR;
         const int rr = t.m0 + r < t.rows ? t.m0 + r : 0;
-        uint32_t srow;
-        if (a.mode == 0)
-            srow = shared ? rr : a.perm[base + rr] / a.k;
-        else
-            srow = shared ? a.T * a.k + rr : base + rr;
-        t.ao[q] = srow * arow_bytes + c16;
+        if constexpr (MODE == 0) {
+            rrs[q] = rr;
+            pv[q] = a.perm[shared ? 0 : base + rr];     // a valid index either way
+        } else {
+            t.ao[q] = uint32_t(shared ? a.T * a.k + rr : base + rr) * arow_bytes + c16;
+        }
+    }
+    if constexpr (MODE == 0) {
+        // the QA perm loads are all issued before the first of them is waited for
+#pragma unroll
+        for (int q = 0; q < QA; ++q) asm volatile("" : "+v"(pv[q]));
+#pragma unroll
+        for (int q = 0; q < QA; ++q)
+            t.ao[q] = (shared ? uint32_t(rrs[q]) : uint32_t(pv[q]) / uint32_t(a.k)) * arow_bytes + c16;
     }
     t.bbase = blob + a.off_w + int64_t(t.n0) * a.K * 2;
     t.obase = (shared ? a.T * a.k : base) + t.m0;
     const int r = tid;
-    t.orow = r >= BM || t.m0 + r >= t.rows ? -1 : a.mode == 0 || shared ? t.obase + r : a.perm[base + t.m0 + r];
+    const bool live = r < BM && t.m0 + r < t.rows;
+    if constexpr (MODE == 0)
+        t.orow = live ? t.obase + r : -1;
+    else
+        t.orow = !live ? -1 : shared ? t.obase + r : a.perm[live && !shared ? base + t.m0 + r : 0];
     return t;
 }
 
@@ -1217,12 +1302,16 @@ __device__ __forceinline__ void bare_barrier() {
 }  // namespace b3
 
 // One tile for a wave that computes FA fragment rows (0..2); slice ks is in buffer (g0 + ks) % 3.
-// On entry slices 0, 1 and 2 have been issued (in that order; the loads still outstanding are
-// at most those three).  On exit every load and store has completed; the caller issues the next
-// tile's slice 2 into buffer (g0 + nk - 1) % 3 (its slices 0 and 1 were issued here).
+// First tile of the workgroup: on entry slices 0, 1 and 2 have been issued, in that order, and
+// nothing else is in flight.  Later tiles: slices 0 and 1 have landed (the previous tile waited
+// for them before its epilogue's stores), and slice 2 and those stores are in flight; the first
+// slice waits for all of them (loads and stores share one completion counter), so the stores
+// drain under its MFMAs.  On exit this tile's stores may be in flight; the caller issues the
+// next tile's slice 2 into buffer (g0 + nk - 1) % 3 (its slices 0 and 1 were issued here).
+// The epilogue also builds nn, the descriptor of tile nn_lid (if >= 0), before its stores.
 template <int MODE, int FA>
 __device__ __forceinline__ void b3_tile(const GemmArgs& a, uint8_t* lds8, const b3::Tile& t, const b3::Tile& nx,
-                                        bool has_next, int g0) {
+                                        bool has_next, int g0, bool first, int nn_lid, b3::Tile& nn) {
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave / b3::WN, wn = wave % b3::WN;
     const int nk = a.K / b3::BK;
@@ -1267,8 +1356,10 @@ __device__ __forceinline__ void b3_tile(const GemmArgs& a, uint8_t* lds8, const 
         }
     };
     bf16x8 fa0[NA], fb0[b3::FN], fa1[NA], fb1[b3::FN];
-    b3::wait_vm<2 * b3::Q>();           // slice 0 landed (slices 1 and 2 may still be in flight)
-    b3::bare_barrier();
+    if (first) {
+        b3::wait_vm<2 * b3::Q>();       // slice 0 landed (slices 1 and 2 may still be in flight)
+        b3::bare_barrier();
+    }
     if (MODE == 1 && tid < b3::BM) reinterpret_cast<int32_t*>(lds8 + b3::ROWTAB)[tid] = t.orow;   // read after later barriers
     if constexpr (FA > 0) frag(lds8 + buf_of(0) * b3::STAGE, 0, fa0, fb0);
     for (int ks = 0; ks + 1 < nk; ++ks) {
@@ -1285,9 +1376,14 @@ __device__ __forceinline__ void b3_tile(const GemmArgs& a, uint8_t* lds8, const 
             sched();
         }
         // every wave has read slice ks (its buffer can take slice ks + 3) and slice ks + 1 has
-        // landed (slice ks + 2, issued one slice later, may still be in flight)
-        b3::wait_vm<b3::Q>();
-        __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): the fragment reads of this wave done
+        // landed (slice ks + 2, issued one slice later, may still be in flight; in the first
+        // slice of a later tile everything in flight is waited for, the previous stores too)
+        if (!first && ks == 0) {
+            __builtin_amdgcn_s_waitcnt(0x0070);      // vmcnt(0) lgkmcnt(0)
+        } else {
+            b3::wait_vm<b3::Q>();
+            __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the fragment reads of this wave done
+        }
         b3::bare_barrier();
         {
             // slice ks + 3 into the buffer slice ks leaves: this tile's, else the next tile's slice
@@ -1316,7 +1412,13 @@ __device__ __forceinline__ void b3_tile(const GemmArgs& a, uint8_t* lds8, const 
     // Epilogue staged in the buffer of the last slice (the next tile's slices 0 and 1 are
     // loading into the other two); afterwards the next tile's slice 2 goes there.
     uint8_t* stg = lds8 + buf_of(nk - 1) * b3::STAGE;
-    __syncthreads();            // every wave is done with slice nk - 1
+    // every wave is done with slice nk - 1, and the next tile's slices 0 and 1 have landed
+    // (only loads are in flight here: the wait costs their tail, before any store is issued)
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    auto next_desc = [&]() {
+        if (nn_lid >= 0) nn = b3::make_tile<MODE>(a, nn_lid, a.N / b3::BN);
+    };
     if (MODE == 0) {
 #pragma unroll
         for (int i = 0; i < FA; ++i)
@@ -1339,15 +1441,22 @@ __device__ __forceinline__ void b3_tile(const GemmArgs& a, uint8_t* lds8, const 
                     *reinterpret_cast<uint16_t*>(stg + r * b3::HSTR + col * 2) = bf16_bits(hv[qq]);
                 }
             }
-        __syncthreads();
+        next_desc();
+        lds_barrier();
         constexpr int CH = b3::BN / 16;
+        constexpr int PER = b3::BM * CH / b3::kThreads;
         uint16_t* h = static_cast<uint16_t*>(a.out);
-#pragma unroll 4
-        for (int idx = tid; idx < b3::BM * CH; idx += b3::kThreads) {
-            const int r = idx / CH, c = idx % CH;
+        dev::u32x4 v[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int idx = tid + k * b3::kThreads, r = idx / CH, c = idx % CH;
+            v[k] = *reinterpret_cast<const dev::u32x4*>(stg + r * b3::HSTR + c * 16);
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int idx = tid + k * b3::kThreads, r = idx / CH, c = idx % CH;
             if (t.m0 + r < t.rows)
-                *reinterpret_cast<dev::u32x4*>(h + int64_t(t.obase + r) * a.I + t.n0 / 2 + c * 8) =
-                    *reinterpret_cast<const dev::u32x4*>(stg + r * b3::HSTR + c * 16);
+                *reinterpret_cast<dev::u32x4*>(h + int64_t(t.obase + r) * a.I + t.n0 / 2 + c * 8) = v[k];
         }
     } else {
         uint16_t* o = static_cast<uint16_t*>(a.out);
@@ -1367,20 +1476,28 @@ __device__ __forceinline__ void b3_tile(const GemmArgs& a, uint8_t* lds8, const 
                         }
                     }
             }
-            __syncthreads();
-#pragma unroll 4
-            for (int idx = tid; idx < b3::BM * 16; idx += b3::kThreads) {
-                const int r = idx / 16, c = idx % 16;
-                const int d = orow[r];
-                if (d >= 0)
-                    *reinterpret_cast<dev::u32x4*>(o + int64_t(d) * a.H + t.n0 + pass * (b3::BN / 2) + c * 8) =
-                        *reinterpret_cast<const dev::u32x4*>(stg + r * b3::HSTR + c * 16);
+            if (pass == 0) next_desc();
+            lds_barrier();
+            // the LDS reads first, then the stores
+            constexpr int PER = b3::BM * 16 / b3::kThreads;
+            int32_t d[PER];
+            dev::u32x4 v[PER];
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int idx = tid + k * b3::kThreads, r = idx / 16, c = idx % 16;
+                d[k] = orow[r];
+                v[k] = *reinterpret_cast<const dev::u32x4*>(stg + r * b3::HSTR + c * 16);
             }
-            if (pass == 0) __syncthreads();
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int c = (tid + k * b3::kThreads) % 16;
+                if (d[k] >= 0)
+                    *reinterpret_cast<dev::u32x4*>(o + int64_t(d[k]) * a.H + t.n0 + pass * (b3::BN / 2) + c * 8) = v[k];
+            }
+            if (pass == 0) lds_barrier();
         }
     }
-    __syncthreads();            // the staging is read
-    __builtin_amdgcn_s_waitcnt(0);   // the stores and every load issued so far have completed
+    lds_barrier();              // the staging is read: the next tile's slice 2 goes into its buffer
 }
 
 template <int MODE>
@@ -1394,31 +1511,35 @@ k_gemm_b3(const GemmArgs a) {
     int i = blockIdx.x / kXcds;
     if (i >= per_xcd || x * per_xcd + i >= total) return;
     const int nk = a.K / b3::BK;
-    // the tile descriptors are read while no slice is in flight (their loads would otherwise
-    // wait for the slices ahead of them)
-    b3::Tile cur = b3::make_tile(a, x * per_xcd + i, n_tiles);
+    // the descriptors of the first two tiles are read while no slice is in flight (their
+    // loads would otherwise wait for the slices ahead of them); later ones in the epilogue two
+    // tiles ahead, before its stores
+    b3::Tile cur = b3::make_tile<MODE>(a, x * per_xcd + i, n_tiles);
     int in = i + stride;
     bool has_next = in < per_xcd && x * per_xcd + in < total;
-    b3::Tile nx = has_next ? b3::make_tile(a, x * per_xcd + in, n_tiles) : cur;
+    b3::Tile nx = has_next ? b3::make_tile<MODE>(a, x * per_xcd + in, n_tiles) : cur;
 #pragma unroll
     for (int s = 0; s < 3; ++s) b3::issue(lds8, a, cur, s, s);
     int g0 = 0;
+    bool first = true;
     while (true) {
+        const int in2 = in + stride;
+        const bool has_next2 = has_next && in2 < per_xcd && x * per_xcd + in2 < total;
+        const int nn_lid = has_next2 ? x * per_xcd + in2 : -1;
+        b3::Tile nn = nx;
         switch (cur.fa) {
-            case 2: b3_tile<MODE, 2>(a, lds8, cur, nx, has_next, g0); break;
-            case 1: b3_tile<MODE, 1>(a, lds8, cur, nx, has_next, g0); break;
-            default: b3_tile<MODE, 0>(a, lds8, cur, nx, has_next, g0); break;
+            case 2: b3_tile<MODE, 2>(a, lds8, cur, nx, has_next, g0, first, nn_lid, nn); break;
+            case 1: b3_tile<MODE, 1>(a, lds8, cur, nx, has_next, g0, first, nn_lid, nn); break;
+            default: b3_tile<MODE, 0>(a, lds8, cur, nx, has_next, g0, first, nn_lid, nn); break;
         }
         if (!has_next) break;
         g0 = (g0 + nk) % 3;
-        i = in;
-        in = i + stride;
-        const bool has_next2 = in < per_xcd && x * per_xcd + in < total;
-        const b3::Tile nn = has_next2 ? b3::make_tile(a, x * per_xcd + in, n_tiles) : nx;
-        b3::issue(lds8, a, nx, 2, (g0 + 2) % 3);       // the new tile's slices 0 and 1 are loaded
+        b3::issue(lds8, a, nx, 2, (g0 + 2) % 3);       // the new tile's slices 0 and 1 have landed
         cur = nx;
         nx = nn;
         has_next = has_next2;
+        in = in2;
+        first = false;
     }
 }
 
@@ -1466,7 +1587,14 @@ int max_tiles(const moe_config& c, int32_t T, int bm) {
 
 }  // namespace
 
-int64_t gemm_tile_ints(const moe_config& c, int32_t T) { return 1 + max_tiles(c, T, BM < dma::BM ? BM : dma::BM); }
+// Tile list: [0] count, [1 .. max] (entry << 16) | m_tile, then from a 16-byte boundary one
+// int4 record per row tile.
+int64_t tile_rec_index(const moe_config& c, int32_t T) {
+    return (1 + int64_t(max_tiles(c, T, BM < dma::BM ? BM : dma::BM)) + 3) / 4 * 4;
+}
+int64_t gemm_tile_ints(const moe_config& c, int32_t T) {
+    return tile_rec_index(c, T) + 4 * int64_t(max_tiles(c, T, BM < dma::BM ? BM : dma::BM));
+}
 
 bool gemm_shape_supported(const moe_config& c) {
     if (c.w_dtype == MOE_W_F32) return false;
@@ -1505,6 +1633,7 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     tm.T = T;
     tm.bm = bm_of(kind1);
     tm.tiles = tiles;
+    tm.rec = reinterpret_cast<int4*>(tiles + tile_rec_index(c, T));
     tm.list = list;
     hipLaunchKernelGGL(k_tile_map, dim3(1), dim3(1024), 0, s, tm);
     hipError_t e = hipGetLastError();
@@ -1516,6 +1645,7 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     a.offsets = offsets;
     a.perm = perm;
     a.tiles = tiles;
+    a.rec = tm.rec;
     a.T = T;
     a.k = c.top_k;
     a.I = c.inter;
