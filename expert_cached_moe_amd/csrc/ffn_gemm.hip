@@ -824,8 +824,9 @@ __device__ __forceinline__ uint32_t b_stride(int K) {
 // Loads of one K slice into stage buffer buf: A rows at a_src + ao[q] + koa (with SKIP, the
 // loads in alive only), weight rows at bbase + boff + kob.  The slice is handed over by a
 // barrier that waits for every load, so the number issued may vary.  Skipping is used by the
-// down GEMM (MXFP4 8K chunk: 843-850 us against 895-899 us); on the gate/up GEMMs it measured
-// no faster (bf16: 458 against 445 us), so they load every row group.
+// down GEMMs (MXFP4 8K chunk: 843-850 us against 895-899 us) and the MXFP4 gate/up GEMM (1,318-
+// 1,320 against 1,331-1,333 us); the bf16 gate/up GEMM measured slower with it (451-454 against
+// 442 us), so it loads every row group.
 template <bool FP4, bool SKIP>
 __device__ __forceinline__ void issue(uint8_t* lds8, const uint8_t* a_src, const uint32_t (&ao)[QA], uint32_t alive,
                                       const uint8_t* bbase, uint32_t boff, uint32_t bstride, uint32_t koa, uint32_t kob,
@@ -986,7 +987,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
     // the accumulators in place across iterations.
     bf16x8 fa0[NA], fb0[big::FN], fa1[NA], fb1[big::FN];
     if (first) barrier_loads();     // slice 0 (and the scales) landed
-    big::issue<FP4, MODE == 1>(lds8, a.a_src, t.ao, t.alive, t.bbase, boff, bstride, big::ROWB, L::BROWB, 1);
+    big::issue<FP4, MODE == 1 || FP4>(lds8, a.a_src, t.ao, t.alive, t.bbase, boff, bstride, big::ROWB, L::BROWB, 1);
     if (MODE == 1 && tid < big::BM) reinterpret_cast<int32_t*>(lds8 + L::ROWTAB)[tid] = t.orow;   // read after later barriers
     if constexpr (FA > 0) frag(lds8, 0, 0, fa0, fb0);
     for (int ks = 0; ks + 1 < nk; ++ks) {
@@ -1016,7 +1017,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
             uint32_t ao[big::QA];
 #pragma unroll
             for (int q = 0; q < big::QA; ++q) ao[q] = other ? nx.ao[q] : t.ao[q];
-            big::issue<FP4, MODE == 1>(lds8, a.a_src, ao, other ? nx.alive : t.alive, other ? nx.bbase : t.bbase, boff, bstride,
+            big::issue<FP4, MODE == 1 || FP4>(lds8, a.a_src, ao, other ? nx.alive : t.alive, other ? nx.bbase : t.bbase, boff, bstride,
                             kn * big::ROWB, kn * L::BROWB,
                             ks & 1);
         }
@@ -1160,7 +1161,7 @@ k_gemm_big(const GemmArgs a) {
     int in = i + stride;
     bool has_next = in < per_xcd && x * per_xcd + in < total;
     big::Tile nx = has_next ? big::make_tile<MODE, FP4>(a, x * per_xcd + in, n_tiles) : cur;
-    big::issue<FP4, MODE == 1>(lds8, a.a_src, cur.ao, cur.alive, cur.bbase, big::b_lane_off<FP4>(a.K), big::b_stride<FP4>(a.K), 0, 0, 0);
+    big::issue<FP4, MODE == 1 || FP4>(lds8, a.a_src, cur.ao, cur.alive, cur.bbase, big::b_lane_off<FP4>(a.K), big::b_stride<FP4>(a.K), 0, 0, 0);
     if (FP4) big::issue_scales(lds8, cur.sbase, a.K);
     bool first = true;
     while (true) {
