@@ -13,10 +13,10 @@
 //
 // Four kernels, chosen per GEMM from N and K:
 //   k_gemm_big  persistent 256 x 256 tiles, K slices of 64 loaded straight into two LDS
-//               stages (bf16 GEMMs with K >= 2048, and every MXFP4 GEMM whose tile scales
+//               stages (bf16 GEMMs with K >= 512, and every MXFP4 GEMM whose tile scales
 //               fit its LDS region);
 //   k_gemm_b3   persistent 128 x 256 tiles, K slices of 64 in a ring of three LDS stages
-//               (the other bf16 GEMMs with at least three slices);
+//               (bf16 GEMMs with K = 256 or 384);
 //   k_gemm_dma  128 x 256 tiles, a ring of 3 stages of K = 32 loaded straight into LDS, two
 //               workgroups per CU (bf16 GEMMs with K = 64 or 128);
 //   k_gemm      register-staged tiles (MXFP4 shapes the large tile does not take).
@@ -1612,10 +1612,10 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
     // kernel per GEMM: 2 large-tile, 3 three-stage 128 x 256, 1 pipelined 128 x 256 (bf16 with
     // fewer than three K slices of 64), 0 register-staged (MXFP4 shapes the large tile does not
     // take; every bf16 shape gemm_shape_supported accepts fits 3 or 1).  The large tile needs
-    // long K loops to pay for its per-tile start and epilogue (measured on the 8K-token chunk of
-    // the 2048 x 768 layer: 547 us against 643 us for the pipelined kernel on GEMM 1 with
-    // K = 2048, about even on GEMM 2 with K = 768); on GEMM 1 the three-stage kernel ran 48 us
-    // slower than the large tile, on GEMM 2 (K = 768) 28 us faster than the pipelined kernel.
+    // K loops long enough to pay for its per-tile start and epilogue; on the 8K-token chunk of
+    // the 2048 x 768 layer it runs GEMM 1 (K = 2048) in 430-438 us against 496 us on the
+    // three-stage kernel, and GEMM 2 (K = 768) in 292-294 us against 300-302 us.  Below K = 512
+    // the three-stage kernel (persistent, two slices of lookahead) takes bf16 GEMMs.
     auto kind = [&](int N, int K) {
         // large tile: an even slice count, A row offsets (rows of x or h times the row bytes)
         // in 32 bits and, for MXFP4, the tile's scales within their LDS region
@@ -1624,7 +1624,7 @@ hipError_t launch_ffn_gemm(const moe_config& c, const BlobLayout& lay, const voi
                             a_rows * K * 2 < (int64_t(1) << 32) && (!fp4 || K <= big::kMaxKFp4);
         if (fp4) return big_ok ? 2 : 0;
         const bool b3_ok = N % b3::BN == 0 && K % b3::BK == 0 && K / b3::BK >= 3 && a_rows * K * 2 < (int64_t(1) << 32);
-        if (K >= 2048 && big_ok) return 2;
+        if (K >= 512 && big_ok) return 2;
         return b3_ok ? 3 : 1;
     };
     auto bm_of = [](int kd) { return kd == 3 ? b3::BM : kd == 2 ? big::BM : kd == 1 ? dma::BM : BM; };

@@ -57,14 +57,15 @@ def test_decode_shape_sweep(B, wdtype, H, I, E, k, T, frac, shared):
 
 
 # Grouped GEMM kernels: large tile for MXFP4 when K <= 4096 and K % 128 == 0, for bf16 when
-# K >= 2048; for the other bf16 GEMMs the three-stage kernel, or the pipelined kernel when K
+# K >= 512; for the other bf16 GEMMs the three-stage kernel, or the pipelined kernel when K
 # has fewer than three slices of 64.  GEMM 1 has N = 2I, K = H; GEMM 2 N = H, K = I.  The
-# three-stage kernel's ring position moves by K / 64 mod 3 per tile: 8, 4, 24 and 10 slices
-# below give 2, 1, 0 and 1.
+# three-stage kernel's ring position moves by K / 64 mod 3 per tile: 4 and 6 slices below
+# give 1 and 0 (the only K it takes are 256 and 384).
 PREFILL = [
-    ("bf16", 512, 128, 8, 2, 37, False),       # three-stage (K = 512) / pipelined (K = 128)
+    ("bf16", 512, 128, 8, 2, 37, False),       # large tile (K = 512) / pipelined (K = 128)
     ("bf16", 2048, 256, 16, 4, 300, True),     # large tile (K = 2048) / three-stage (K = 256)
-    ("bf16", 1536, 640, 8, 3, 130, False),     # three-stage / three-stage, 5 and 6 column tiles
+    ("bf16", 1536, 640, 8, 3, 130, False),     # large tile / large tile, 5 and 6 column tiles
+    ("bf16", 256, 384, 8, 2, 12288, True),     # three-stage (K = 256) / three-stage (K = 384); 864 and 288 tiles: several a workgroup
     ("mxfp4", 1024, 384, 8, 2, 77, False),     # large tile / large tile, K = 1024 and 384
     ("mxfp4", 4096, 2048, 8, 2, 50, True),     # large tile / large tile, K = 4096 and 2048
     ("mxfp4", 512, 1152, 8, 2, 65, False),     # large tile / large tile, 9 column tiles of GEMM 1
