@@ -333,10 +333,10 @@ def test_prefill_mxfp4_register_staged(B, H, I):
 
 
 def test_prefill_bf16_large_tile_down(B):
-    """bf16 prefill with an intermediate size of 2048: the down GEMM (K = I = 2048) runs the
-    large-tile kernel (the workloads' bf16 down GEMMs have K = 768 and run the pipelined one),
-    the gate/up GEMM (K = H = 1024) the pipelined kernel.  Ragged 40-token batch with a shared
-    expert, so tiles end part way and the pair-output rows come from the row table."""
+    """bf16 prefill with an intermediate size of 2048: both GEMMs run the large-tile kernel
+    (K = I = 2048 for the down GEMM, K = H = 1024 for gate/up) on a ragged 40-token batch with
+    a shared expert, so every tile ends part way, the down GEMM skips the A loads of dead row
+    groups and its pair-output rows come from the row table."""
     print("[prefill-bf16-big-down] H=1024 I=2048", flush=True)
     base = synth.workload("v4flash_decode_bf16")
     wl = dataclasses.replace(base, name="bf16_1024x2048", H=1024, I=2048, E=8, k=2, C=8, T=40)
