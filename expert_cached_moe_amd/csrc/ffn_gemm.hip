@@ -1038,8 +1038,8 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, uint8_t* lds8, const
         mma(fa1, fb1);
     }
 
-    // Epilogue through the LDS above buffer 0 (buffer 0 is taking the next tile's first
-    // slice): the tile is staged there and written out as whole rows, 16 bytes a lane.
+    // Epilogue through the LDS above buffer 0 (buffer 0 holds the next tile's first slice):
+    // the tile is staged there and written out as whole rows, 16 bytes a lane.
     uint8_t* stg = lds8 + L::EPI;
     // Every wave is done with slice nk - 1 (buffer 1) and the scales, and the next tile's slice
     // 0 has landed: the only vector memory operations in flight are loads here, so this wait
@@ -1410,8 +1410,8 @@ __device__ __forceinline__ void b3_tile(const GemmArgs& a, uint8_t* lds8, const 
         mma(fa0, fb0);
         mma(fa1, fb1);
     }
-    // Epilogue staged in the buffer of the last slice (the next tile's slices 0 and 1 are
-    // loading into the other two); afterwards the next tile's slice 2 goes there.
+    // Epilogue staged in the buffer of the last slice (the next tile's slices 0 and 1 are in
+    // the other two); afterwards the next tile's slice 2 goes there.
     uint8_t* stg = lds8 + buf_of(nk - 1) * b3::STAGE;
     // every wave is done with slice nk - 1, and the next tile's slices 0 and 1 have landed
     // (only loads are in flight here: the wait costs their tail, before any store is issued)
