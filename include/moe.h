@@ -49,7 +49,7 @@ extern "C" {
 #define MOE_ESHAPE (-2)        /* shape not supported by the config or the kernels */
 #define MOE_ECAPACITY (-3)     /* caller array too small */
 #define MOE_EHIP (-4)          /* a HIP runtime call failed; moe_last_error has its string */
-#define MOE_EUNSUPPORTED (-5)  /* valid request that this build does not implement */
+#define MOE_EUNSUPPORTED (-5)  /* valid request that this library does not implement */
 #define MOE_ESTATE (-6)        /* pools not bound, or a call out of order */
 
 /* weight element formats */
